@@ -1,0 +1,263 @@
+"""Throughput of the KV-compression event on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--cpu-heads N]
+
+One step = one compression event over every head-event of the workload
+(all layers x batch x KV heads): window score -> mass/segmentation/quota ->
+select -> gather, inputs resident in HBM, outputs preallocated.  The default
+workload is the Qwen-7B-shaped decode event (28 layers x 16 sequences x 4 KV
+heads, G=7, d=128, T=768 = budget 256 + a 512-token interval, W=128).
+Inputs are seeded synthetic data (eviction_window_qk_amd.synth).
+
+Prints ONE JSON line:
+  value          cached tokens scored per second (n_heads * T / step time)
+  roofline       the score stage (the dominant kernels: row statistics,
+                 column sums, fill) timed live with HIP events on the launch
+                 stream: algorithmic flops (one causal QK^T) / duration,
+                 against the bf16 dense MFMA peak
+  cpu_baseline   the CPU oracle (test infrastructure, not tuned) timed on this
+                 host's cores on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV-compression throughput: cached tokens scored/sec per GPU; % of roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def _gen_chunk(args):
+    name, heads, seed = args
+    from eviction_window_qk_amd import synth
+    return synth.gen_heads(synth.WORKLOADS[name], heads, seed=seed)
+
+
+def generate(name: str, seed=None, workers: int = 16):
+    """All heads of the workload as bf16 bits (host), in parallel chunks."""
+    from eviction_window_qk_amd import synth
+    wl = synth.WORKLOADS[name]
+    heads = list(range(wl.n_heads))
+    chunks = [heads[i:i + 64] for i in range(0, len(heads), 64)]
+    G, W, d, T = wl.group, wl.window, wl.head_dim, wl.T
+    q = np.empty((wl.n_heads, G, W, d), np.uint16)
+    k = np.empty((wl.n_heads, T, d), np.uint16)
+    v = np.empty((wl.n_heads, T, d), np.uint16)
+    if workers <= 1 or len(chunks) == 1:
+        parts = map(_gen_chunk, [(name, c, seed) for c in chunks])
+    else:
+        import multiprocessing as mp
+        pool = mp.get_context("spawn").Pool(workers)
+        parts = pool.imap(_gen_chunk, [(name, c, seed) for c in chunks])
+    for c, (qq, kk, vv) in zip(chunks, parts):
+        q[c[0]:c[-1] + 1], k[c[0]:c[-1] + 1], v[c[0]:c[-1] + 1] = qq, kk, vv
+    if workers > 1 and len(chunks) > 1:
+        pool.close()
+        pool.join()
+    return q, k, v
+
+
+def algorithmic(wl) -> dict:
+    """Per-event algorithmic work (one causal QK^T; bytes of the data each
+    stage must move at least once)."""
+    NH, G, W, d, T, K = wl.n_heads, wl.group, wl.window, wl.head_dim, wl.T, wl.budget
+    pairs = W * (T - W) + W * (W + 1) // 2           # causal (query, key) pairs per head
+    flops = 2.0 * d * G * pairs * NH
+    ema = bool(wl.params.get("ema"))
+    b_score = NH * (2.0 * T * d + 2.0 * G * W * d + 4.0 * T)
+    b_mass = NH * (4.0 * T + 4.0 * T + (8.0 * K + 16.0 * T if ema else 0.0))
+    b_select = NH * (4.0 * T + 4.0 * K)
+    b_gather = NH * (8.0 * K * d + (16.0 * K if ema else 0.0))
+    return dict(flops=flops, b_score=b_score, b_mass=b_mass, b_select=b_select,
+                b_gather=b_gather, b_total=b_score + b_mass + b_select + b_gather)
+
+
+def _oracle_head(args):
+    name, n = args
+    from eviction_window_qk_amd import synth
+    from oracle import ams
+    wl = synth.WORKLOADS[name]
+    hd = synth.gen_head(wl, n)
+    pd = wl.event_params()
+    keys = set(ams.Params.__dataclass_fields__)
+    op = ams.Params(**{k: v for k, v in pd.items() if k in keys})
+    q = synth.bf16_bits_to_f32(hd["q"]).astype(np.float64)
+    k = synth.bf16_bits_to_f32(hd["k"]).astype(np.float64)
+    t0 = time.perf_counter()
+    ams.event(q, k, hd["v"], None, op)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(name: str, n_heads: int, cores: int) -> dict:
+    """The oracle, as it stands, on the first n_heads heads of the workload."""
+    import multiprocessing as mp
+    from eviction_window_qk_amd import synth
+    wl = synth.WORKLOADS[name]
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    heads = list(range(min(n_heads, wl.n_heads)))
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_head, [(name, 0)] * cores)           # warm the workers
+        t0 = time.perf_counter()
+        busy = pool.map(_oracle_head, [(name, n) for n in heads])
+        wall = time.perf_counter() - t0
+    tokens = len(heads) * wl.T
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(heads)} of {wl.n_heads} head-events of {name} (T={wl.T}), full "
+                      f"oracle event per head (fp64 score + exact steps 2-5), {cores} worker "
+                      f"processes x 1 thread; {sum(busy):.1f} s of CPU work in {wall:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen7b_t768")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (the event is independent per head "
+              f"and runs on one GPU's share); --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from eviction_window_qk_amd import kvc, synth
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py: no GPU visible")
+    wl = synth.WORKLOADS[args.workload]
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    t_gen = time.perf_counter()
+    q, k, v = generate(args.workload, workers=cores)
+    print(f"[bench] generated {wl.n_heads} head-events in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    del q, k, v
+    ema = bool(wl.params.get("ema"))
+    n_prev = wl.budget if ema else 0
+    p = kvc.Params.from_dict(wl.event_params(), n_heads=wl.n_heads, n_prev=n_prev)
+    credit = None
+    if ema:  # carried credit from a prior event: uniform mass over the kept slots
+        credit = torch.full((wl.n_heads, n_prev), (1 << 44) // n_prev, dtype=torch.int64,
+                            device=dev)
+    ws = kvc.new_workspace(p, dev)
+    S = kvc.segment_capacity(p)
+    u = torch.empty((wl.n_heads, wl.T), dtype=torch.float32, device=dev)
+    out = dict(score=torch.empty((wl.n_heads, wl.T), dtype=torch.float32, device=dev),
+               seg_start=torch.empty((wl.n_heads, S), dtype=torch.int32, device=dev),
+               seg_quota=torch.empty((wl.n_heads, S), dtype=torch.int32, device=dev),
+               n_seg=torch.empty((wl.n_heads,), dtype=torch.int32, device=dev))
+    if ema:
+        out["credit_upd"] = torch.empty((wl.n_heads, wl.T), dtype=torch.int64, device=dev)
+    kept = torch.empty((wl.n_heads, wl.budget), dtype=torch.int32, device=dev)
+    k_out = torch.empty((wl.n_heads, wl.budget, wl.head_dim), dtype=torch.bfloat16, device=dev)
+    v_out = torch.empty_like(k_out)
+    c_out = torch.empty((wl.n_heads, wl.budget), dtype=torch.int64, device=dev) if ema else None
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        kvc.score_window(p, dq, dk, u=u, ws=ws, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        kvc.mass_segment(p, u, credit, ws=ws, stream=stream, out=out)
+        if ev:
+            ev[2].record(stream)
+        kvc.select(p, out["score"], out["seg_start"], out["seg_quota"], out["n_seg"], kept=kept,
+                   ws=ws, stream=stream)
+        if ev:
+            ev[3].record(stream)
+        kvc.gather_compact(p, kept, dk, dv, out.get("credit_upd"), k_out=k_out, v_out=v_out,
+                           credit_out=c_out, stream=stream)
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms = total_ms / args.steps
+    stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])
+    stage_ms = stage.mean(axis=0)
+
+    # The whole-event entry point on the same data, for reference.
+    for _ in range(2):
+        kvc.compress_event(p, dq, dk, dv, credit, ws=ws, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        kvc.compress_event(p, dq, dk, dv, credit, ws=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    event_ms = e0.elapsed_time(e1) / args.steps
+
+    alg = algorithmic(wl)
+    tokens = wl.n_heads * wl.T
+    score_s = stage_ms[0] * 1e-3
+    achieved = alg["flops"] / score_s / 1e12
+    t_roof = max(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12), alg["b_total"] / (PEAK_HBM_GBS * 1e9))
+    gather_gbs = alg["b_gather"] / (stage_ms[3] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_heads": wl.n_heads, "layers": wl.layers,
+                   "batch": wl.batch, "kv_heads": wl.kv_heads, "group": wl.group,
+                   "head_dim": wl.head_dim, "T": wl.T, "window": wl.window,
+                   "budget": wl.budget, "ema": ema, "seed": wl.seed},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "score stage (k_rowstats + k_colsum + k_fill)",
+                     "algorithmic_flops_per_launch": alg["flops"]},
+        "events_per_s": 1000.0 / ms,
+        "event_roofline_frac": t_roof / (ms * 1e-3),
+        "event_entry_ms": event_ms,
+        "stages_ms": {"score": stage_ms[0], "mass_segment": stage_ms[1],
+                      "select": stage_ms[2], "gather": stage_ms[3]},
+        "gather": {"achieved_GBs": gather_gbs, "frac": gather_gbs / PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_heads, cores)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

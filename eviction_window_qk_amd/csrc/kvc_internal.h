@@ -1,0 +1,56 @@
+// Internal declarations shared by the libkvc translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr int kUsageShift = 40;        // usage fixed point: trunc(ubar * 2^40)
+constexpr int kCreditShift = 44;       // credit and mixed-mass fixed point (Q44)
+constexpr int kMaxRows = 4096;         // W * G
+constexpr int kMaxT = 1 << 18;         // keep-mask bitmap fits one workgroup's LDS
+constexpr int kMaxThresholds = 1024;   // mass cuts per head
+constexpr int kScoreKeysPerWave = 64;  // two 32-key MFMA blocks per wave
+constexpr int kScoreWaves = 4;
+constexpr int kScoreChunk = kScoreKeysPerWave * kScoreWaves;  // keys per workgroup
+
+// Parameters after validation, with every derived quantity the kernels need.
+struct Derived {
+  int NH, G, D, T, TS, W, K, R;
+  int n_chunks;                 // score key chunks per head
+  int seg_min, seg_max, q_min;
+  int s_keep, r_keep, t_keep;   // S', R', budget left after must-keep
+  int pool_h, pool_mode, head_agg, ema, n_prev;
+  int n_thr, s_cap;
+  float c_log2;                 // softmax scale * log2(e)
+  uint64_t eps_q;               // ceil(eps * 2^40)
+  double delta, lam, oml, beta, omb;
+};
+
+// Workspace carve-up (byte offsets into the caller's buffer, 256-B aligned).
+struct WsLayout {
+  size_t stats, u, score, cupd, vp, seg_start, seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q,
+      ends, total;
+};
+WsLayout workspace_layout(const Derived& d);
+
+// Launchers (one per translation unit); return the first HIP error.
+hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u, float* stats,
+                        hipStream_t s);
+hipError_t launch_mass_segment(const Derived& d, const float* u, const uint64_t* credit_in,
+                               float* score, uint64_t* credit_upd, uint64_t* vp,
+                               int32_t* seg_start, int32_t* seg_quota, int32_t* n_seg,
+                               uint64_t* seg_m, int32_t* seg_a, int32_t* seg_f, int32_t* seg_q,
+                               int32_t* ends, hipStream_t s);
+hipError_t launch_select(const Derived& d, const float* score, const int32_t* seg_start,
+                         const int32_t* seg_quota, const int32_t* n_seg, int32_t* kept,
+                         hipStream_t s);
+hipError_t launch_gather(const Derived& d, const int32_t* kept, const void* k, const void* v,
+                         const uint64_t* credit_upd, void* k_out, void* v_out,
+                         uint64_t* credit_out, hipStream_t s);
+
+}  // namespace kvc

@@ -1,0 +1,294 @@
+// Step 4 on gfx950: in-segment top-q, union with must-keep, budget repair and
+// sorted kept indices.  One workgroup per head-event; the keep set lives as a
+// bitmap in LDS.
+//
+// Sources: AMS notes, key design 3 (last paragraph: union with the must-keep
+// set, duplicates counted once; over budget drop low-score non-must-keep
+// positions, under budget add high-score unselected ones) and key design 4
+// (per-segment top-k on the base score, kept indices sorted).
+//
+// Ranking is by (score desc, position asc).  Scores become order-preserving
+// 32-bit keys (+0 and -0 equal), so "the r best of a set" is exact integer
+// work: the largest key tau with at least r members >= tau (a bit-by-bit
+// search, one population count per bit), then the members above tau and the
+// lowest-positioned members equal to tau up to r.  The result is the unique
+// canonical selection, independent of thread order.
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kWaveSeg = 256;  // segments up to this length: one wave each
+constexpr int kPerLane = kWaveSeg / 64;
+
+struct Shared {
+  uint32_t bits[kMaxT / 32];
+  uint32_t red[kWaves];
+};
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) == 0) return 0x80000000u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ bool test_bit(const Shared& sh, int t) {
+  return (sh.bits[t >> 5] >> (t & 31)) & 1u;
+}
+
+__device__ __forceinline__ void set_bit(Shared& sh, int t) {
+  atomicOr(&sh.bits[t >> 5], 1u << (t & 31));
+}
+
+__device__ __forceinline__ void clear_bit(Shared& sh, int t) {
+  atomicAnd(&sh.bits[t >> 5], ~(1u << (t & 31)));
+}
+
+// Block-wide count; every thread must call it.
+__device__ uint32_t block_count(uint32_t c, Shared& sh) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) s += sh.red[i];
+  return s;
+}
+
+// The r best positions of {t in [a,b] : pred(t)} are those with key > tau,
+// plus those with key == tau and t <= xcut.  Requires 1 <= r < |set|; every
+// thread must call it with the same arguments.
+template <class Pred>
+__device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint32_t r, Pred pred,
+                                Shared& sh, uint32_t* tau_out, int* xcut_out) {
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    uint32_t c = 0;
+    for (int t = a + threadIdx.x; t <= b; t += kThreads)
+      c += (pred(t) && order_key(sc[t]) >= cand) ? 1u : 0u;
+    if (block_count(c, sh) >= r) tau = cand;
+  }
+  uint32_t c = 0;
+  for (int t = a + threadIdx.x; t <= b; t += kThreads)
+    c += (pred(t) && order_key(sc[t]) > tau) ? 1u : 0u;
+  const uint32_t need = r - block_count(c, sh);
+  int lo = a, hi = b;
+  while (lo < hi) {
+    const int mid = lo + ((hi - lo) >> 1);
+    uint32_t e = 0;
+    for (int t = a + threadIdx.x; t <= mid; t += kThreads)
+      e += (pred(t) && order_key(sc[t]) == tau) ? 1u : 0u;
+    if (block_count(e, sh) >= need) hi = mid; else lo = mid + 1;
+  }
+  *tau_out = tau;
+  *xcut_out = lo;
+}
+
+__device__ __forceinline__ uint32_t wave_count(bool v) { return __popcll(__ballot(v)); }
+
+__global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __restrict__ score,
+                                                     const int32_t* __restrict__ seg_start,
+                                                     const int32_t* __restrict__ seg_quota,
+                                                     const int32_t* __restrict__ n_seg,
+                                                     int32_t* __restrict__ kept) {
+  __shared__ Shared sh;
+  const int n = blockIdx.x;
+  const int T = P.T, K = P.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* kn = kept + size_t(n) * K;
+  if (T <= K) {  // nothing to evict: identity, -1 past T
+    for (int j = tid; j < K; j += kThreads) kn[j] = j < T ? j : -1;
+    return;
+  }
+  const float* sc = score + size_t(n) * T;
+  const int nw = (T + 31) >> 5;
+  const int s_keep = P.s_keep, r_beg = T - P.r_keep;
+  auto must_keep = [&](int t) { return t < s_keep || t >= r_beg; };
+
+  for (int w = tid; w < nw; w += kThreads) sh.bits[w] = 0;
+  __syncthreads();
+  for (int t = tid; t < s_keep; t += kThreads) set_bit(sh, t);
+  for (int t = r_beg + tid; t < T; t += kThreads) set_bit(sh, t);
+
+  // Segments as given (sanitised to [0,T); empty ones are skipped).
+  int ns = n_seg[n];
+  ns = ns < 0 ? 0 : (ns > P.s_cap ? P.s_cap : ns);
+  const int32_t* ss = seg_start + size_t(n) * P.s_cap;
+  const int32_t* sq = seg_quota + size_t(n) * P.s_cap;
+  auto seg_bounds = [&](int i, int* a, int* b) {
+    int s0 = ss[i], s1 = i + 1 < ns ? ss[i + 1] : T;
+    s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
+    s1 = s1 < 0 ? 0 : (s1 > T ? T : s1);
+    *a = s0;
+    *b = s1 - 1;
+  };
+
+  // Long segments: the whole workgroup, one at a time.
+  for (int i = 0; i < ns; ++i) {
+    int a, b;
+    seg_bounds(i, &a, &b);
+    if (b - a + 1 <= kWaveSeg) continue;
+    const int q = sq[i] < 0 ? 0 : sq[i];
+    uint32_t c = 0;
+    for (int t = a + tid; t <= b; t += kThreads) c += must_keep(t) ? 0u : 1u;
+    const uint32_t avail = block_count(c, sh);
+    if (q == 0 || avail == 0) continue;
+    if (uint32_t(q) >= avail) {
+      for (int t = a + tid; t <= b; t += kThreads)
+        if (!must_keep(t)) set_bit(sh, t);
+      continue;
+    }
+    uint32_t tau;
+    int xcut;
+    block_threshold(sc, a, b, uint32_t(q), [&](int t) { return !must_keep(t); }, sh, &tau, &xcut);
+    for (int t = a + tid; t <= b; t += kThreads) {
+      if (must_keep(t)) continue;
+      const uint32_t kk = order_key(sc[t]);
+      if (kk > tau || (kk == tau && t <= xcut)) set_bit(sh, t);
+    }
+  }
+
+  // Short segments: one wave each, keys held in registers.
+  for (int i = wave; i < ns; i += kWaves) {
+    int a, b;
+    seg_bounds(i, &a, &b);
+    const int L = b - a + 1;
+    if (L <= 0 || L > kWaveSeg) continue;
+    const int q = sq[i] < 0 ? 0 : sq[i];
+    if (q == 0) continue;
+    bool ok[kPerLane];
+    uint32_t key[kPerLane];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) {
+      const int t = a + lane + 64 * e;
+      ok[e] = t <= b && !must_keep(t);
+      key[e] = ok[e] ? order_key(sc[t]) : 0u;
+      avail += wave_count(ok[e]);
+    }
+    if (uint32_t(q) >= avail) {
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e)
+        if (ok[e]) set_bit(sh, a + lane + 64 * e);
+      continue;
+    }
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) c += wave_count(ok[e] && key[e] >= cand);
+      if (c >= uint32_t(q)) tau = cand;
+    }
+    uint32_t gt = 0;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) gt += wave_count(ok[e] && key[e] > tau);
+    const uint32_t need = uint32_t(q) - gt;
+    // Positions a+lane+64e in ascending order are e-major, lane-minor: walk
+    // the ties in that order and take the first `need`.
+    uint32_t taken = 0;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) {
+      const bool tie = ok[e] && key[e] == tau;
+      const uint64_t m = __ballot(tie);
+      const uint32_t before = __popcll(m & ((uint64_t(1) << lane) - 1));
+      const bool take = ok[e] && (key[e] > tau || (tie && taken + before < need));
+      if (take) set_bit(sh, a + lane + 64 * e);
+      taken += __popcll(m);
+    }
+  }
+  __syncthreads();
+
+  // Budget repair.
+  uint32_t c = 0;
+  for (int w = tid; w < nw; w += kThreads) c += __popc(sh.bits[w]);
+  const uint32_t n_keep = block_count(c, sh);
+  const uint32_t n_mk = uint32_t(s_keep + P.r_keep);
+  if (n_keep > uint32_t(K)) {
+    // Keep the best K - |MK| picks, drop the rest (the lowest-scored first).
+    auto is_pick = [&](int t) { return !must_keep(t) && test_bit(sh, t); };
+    const uint32_t r = uint32_t(K) - n_mk;
+    if (r == 0) {
+      __syncthreads();
+      for (int t = tid; t < T; t += kThreads)
+        if (!must_keep(t)) clear_bit(sh, t);
+    } else {
+      uint32_t tau;
+      int xcut;
+      block_threshold(sc, 0, T - 1, r, is_pick, sh, &tau, &xcut);
+      // Each thread tests and clears only its own positions' bits.
+      __syncthreads();
+      for (int t = tid; t < T; t += kThreads) {
+        if (must_keep(t) || !test_bit(sh, t)) continue;
+        const uint32_t kk = order_key(sc[t]);
+        if (!(kk > tau || (kk == tau && t <= xcut))) clear_bit(sh, t);
+      }
+    }
+  } else if (n_keep < uint32_t(K)) {
+    // Add the best unselected positions.
+    auto is_free = [&](int t) { return !must_keep(t) && !test_bit(sh, t); };
+    const uint32_t r = uint32_t(K) - n_keep;
+    uint32_t f = 0;
+    for (int t = tid; t < T; t += kThreads) f += is_free(t) ? 1u : 0u;
+    const uint32_t n_free = block_count(f, sh);
+    if (r >= n_free) {
+      __syncthreads();
+      for (int t = tid; t < T; t += kThreads)
+        if (!must_keep(t)) set_bit(sh, t);
+    } else {
+      uint32_t tau;
+      int xcut;
+      block_threshold(sc, 0, T - 1, r, is_free, sh, &tau, &xcut);
+      // Each thread tests and sets only its own positions' bits.
+      __syncthreads();
+      for (int t = tid; t < T; t += kThreads) {
+        if (!is_free(t)) continue;
+        const uint32_t kk = order_key(sc[t]);
+        if (kk > tau || (kk == tau && t <= xcut)) set_bit(sh, t);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Compaction: ascending positions of the set bits.
+  const int wpt = (nw + kThreads - 1) / kThreads;
+  const int w0 = tid * wpt;
+  uint32_t cnt = 0;
+  for (int w = w0; w < w0 + wpt && w < nw; ++w) cnt += __popc(sh.bits[w]);
+  uint32_t incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) sh.red[wave] = incl;
+  __syncthreads();
+  uint32_t pos = incl - cnt;
+  for (int i = 0; i < wave; ++i) pos += sh.red[i];
+  for (int w = w0; w < w0 + wpt && w < nw; ++w) {
+    uint32_t word = sh.bits[w];
+    while (word) {
+      const int b = __ffs(word) - 1;
+      word &= word - 1;
+      if (pos < uint32_t(K)) kn[pos] = w * 32 + b;
+      ++pos;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const Derived& d, const float* score, const int32_t* seg_start,
+                         const int32_t* seg_quota, const int32_t* n_seg, int32_t* kept,
+                         hipStream_t s) {
+  k_select<<<d.NH, kThreads, 0, s>>>(d, score, seg_start, seg_quota, n_seg, kept);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,337 @@
+"""Thin Python binding over libkvc (include/kvc.h): argument marshalling only.
+
+Every step of the event runs in the HIP library; this module checks tensor
+dtypes, devices, shapes and contiguity, passes raw device pointers and the
+current HIP stream, and turns status codes into exceptions.  PyTorch is used
+for device memory and streams only.  There is no fallback: if the library is
+missing or fails to load, every call raises.
+
+Tensor conventions (see include/kvc.h for the full layouts):
+  bf16 data     torch.bfloat16 (or torch.uint16 / torch.int16 bit views)
+  u64 credit    torch.int64 holding the unsigned bit pattern
+  i32 indices   torch.int32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, fields
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+OK, NOOP = 0, 1
+POOL_AVG, POOL_MAX = 0, 1
+AGG_SUM, AGG_MAX = 0, 1
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: status {status}: {strerror(status)}")
+
+
+class _CParams(ctypes.Structure):
+    _fields_ = [
+        ("n_heads", ctypes.c_int32), ("group", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("T", ctypes.c_int32), ("t_stride", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("budget", ctypes.c_int32), ("seg_min", ctypes.c_int32), ("seg_max", ctypes.c_int32),
+        ("q_min", ctypes.c_int32), ("sinks", ctypes.c_int32), ("recent", ctypes.c_int32),
+        ("pool_kernel", ctypes.c_int32), ("pool_mode", ctypes.c_int32),
+        ("head_agg", ctypes.c_int32), ("ema", ctypes.c_int32), ("n_prev", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("delta", ctypes.c_double), ("lambda_", ctypes.c_double),
+        ("beta", ctypes.c_double), ("eps", ctypes.c_double),
+    ]
+
+
+@dataclass
+class Params:
+    """Mirror of kvc_params (names follow the pages' quantities)."""
+    n_heads: int
+    T: int
+    window: int
+    budget: int
+    group: int = 1
+    head_dim: int = 128
+    t_stride: int = 0          # 0 => T
+    delta: float = 0.1
+    seg_min: int = 16
+    seg_max: int = 256
+    q_min: int = 1
+    sinks: int = 4
+    recent: int = 64
+    pool_kernel: int = 7
+    pool_mode: int = POOL_AVG
+    head_agg: int = AGG_SUM
+    ema: bool = False
+    lam: float = 0.9
+    beta: float = 0.9
+    eps: float = 1e-6
+    n_prev: int = 0
+    scale: float = 0.0
+
+    @classmethod
+    def from_dict(cls, d: dict, **over) -> "Params":
+        names = {f.name for f in fields(cls)}
+        kw = {k: v for k, v in {**d, **over}.items() if k in names}
+        return cls(**kw)
+
+    def to_c(self) -> _CParams:
+        c = _CParams()
+        for f in fields(self):
+            v = getattr(self, f.name)
+            if f.name == "lam":
+                c.lambda_ = float(v)
+            elif f.name == "t_stride":
+                c.t_stride = int(v) if v else int(self.T)
+            elif f.name == "ema":
+                c.ema = 1 if v else 0
+            elif f.name in ("delta", "beta", "eps", "scale"):
+                setattr(c, f.name, float(v))
+            else:
+                setattr(c, f.name, int(v))
+        return c
+
+    @property
+    def stride(self) -> int:
+        return self.t_stride or self.T
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libkvc.so not found at {LIB_PATH}: build it with "
+                           "`python -m eviction_window_qk_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(_CParams)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "kvc_score_window": [P, vp, vp, vp, vp, sz, vp],
+        "kvc_mass_segment": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "kvc_select": [P, vp, vp, vp, vp, vp, vp, sz, vp],
+        "kvc_gather_compact": [P, vp, vp, vp, vp, vp, vp, vp, vp],
+        "kvc_compress_event": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "kvc_workspace_bytes": [P],
+        "kvc_segment_capacity": [P],
+        "kvc_check_params": [P],
+        "kvc_strerror": [ctypes.c_int],
+        "kvc_abi_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.kvc_workspace_bytes.restype = ctypes.c_size_t
+    L.kvc_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().kvc_strerror(status).decode()
+
+
+def abi_version() -> int:
+    return lib().kvc_abi_version()
+
+
+def check_params(p: Params) -> int:
+    c = p.to_c()
+    return lib().kvc_check_params(ctypes.byref(c))
+
+
+def workspace_bytes(p: Params) -> int:
+    c = p.to_c()
+    return int(lib().kvc_workspace_bytes(ctypes.byref(c)))
+
+
+def segment_capacity(p: Params) -> int:
+    c = p.to_c()
+    rc = lib().kvc_segment_capacity(ctypes.byref(c))
+    if rc < 0:
+        raise KvcError(rc, "kvc_segment_capacity")
+    return rc
+
+
+# ---------------------------------------------------------------------------
+# tensor plumbing
+# ---------------------------------------------------------------------------
+
+_BF16_LIKE = (torch.bfloat16, torch.uint16, torch.int16)
+
+
+def _ptr(t, dtypes, shape, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int, fn: str) -> int:
+    if rc < 0:
+        raise KvcError(rc, fn)
+    return rc
+
+
+def _device(*ts):
+    for t in ts:
+        if isinstance(t, torch.Tensor):
+            return t.device
+    raise ValueError("no tensor argument")
+
+
+def new_workspace(p: Params, device) -> torch.Tensor:
+    n = workspace_bytes(p)
+    if n == 0:
+        raise KvcError(_check_params_rc(p), "kvc_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _check_params_rc(p: Params) -> int:
+    rc = check_params(p)
+    return rc if rc < 0 else -1
+
+
+def _ws(p, ws, device):
+    if ws is None:
+        ws = new_workspace(p, device)
+    if ws.dtype != torch.uint8 or ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace: contiguous uint8 GPU tensor expected")
+    return ws
+
+
+def score_window(p: Params, q, k, u=None, ws=None, stream=None):
+    """Step 1.  q [NH,G,W,d] bf16, k [NH,t_stride,d] bf16 -> u [NH,T] fp32."""
+    dev = _device(q, k)
+    if u is None:
+        u = torch.empty((p.n_heads, p.T), dtype=torch.float32, device=dev)
+    ws = _ws(p, ws, dev)
+    c = p.to_c()
+    rc = lib().kvc_score_window(
+        ctypes.byref(c),
+        _ptr(q, _BF16_LIKE, (p.n_heads, p.group, p.window, p.head_dim), "q_win"),
+        _ptr(k, _BF16_LIKE, (p.n_heads, p.stride, p.head_dim), "k"),
+        _ptr(u, (torch.float32,), (p.n_heads, p.T), "u"), ws.data_ptr(), ws.numel(),
+        _stream(stream))
+    _check(rc, "kvc_score_window")
+    return u
+
+
+def mass_segment(p: Params, u, credit_in=None, ws=None, stream=None, out=None):
+    """Steps 2-3.  Returns dict(score, credit_upd, seg_start, seg_quota, n_seg, status)."""
+    dev = _device(u)
+    S = segment_capacity(p)
+    o = dict(out or {})
+    o.setdefault("score", torch.empty((p.n_heads, p.T), dtype=torch.float32, device=dev))
+    if p.ema:
+        o.setdefault("credit_upd", torch.empty((p.n_heads, p.T), dtype=torch.int64, device=dev))
+    o.setdefault("seg_start", torch.empty((p.n_heads, S), dtype=torch.int32, device=dev))
+    o.setdefault("seg_quota", torch.empty((p.n_heads, S), dtype=torch.int32, device=dev))
+    o.setdefault("n_seg", torch.empty((p.n_heads,), dtype=torch.int32, device=dev))
+    ws = _ws(p, ws, dev)
+    c = p.to_c()
+    rc = lib().kvc_mass_segment(
+        ctypes.byref(c), _ptr(u, (torch.float32,), (p.n_heads, p.T), "u"),
+        _ptr(credit_in, (torch.int64,), (p.n_heads, p.n_prev), "credit_in"),
+        _ptr(o["score"], (torch.float32,), (p.n_heads, p.T), "score"),
+        _ptr(o.get("credit_upd"), (torch.int64,), (p.n_heads, p.T), "credit_upd"),
+        _ptr(o["seg_start"], (torch.int32,), (p.n_heads, S), "seg_start"),
+        _ptr(o["seg_quota"], (torch.int32,), (p.n_heads, S), "seg_quota"),
+        _ptr(o["n_seg"], (torch.int32,), (p.n_heads,), "n_seg"), ws.data_ptr(), ws.numel(),
+        _stream(stream))
+    o["status"] = _check(rc, "kvc_mass_segment")
+    return o
+
+
+def select(p: Params, score, seg_start, seg_quota, n_seg, kept=None, ws=None, stream=None):
+    """Step 4.  Returns kept [NH, budget] int32 (ascending, -1 padded)."""
+    dev = _device(score)
+    S = segment_capacity(p)
+    if kept is None:
+        kept = torch.empty((p.n_heads, p.budget), dtype=torch.int32, device=dev)
+    ws = _ws(p, ws, dev)
+    c = p.to_c()
+    rc = lib().kvc_select(
+        ctypes.byref(c), _ptr(score, (torch.float32,), (p.n_heads, p.T), "score"),
+        _ptr(seg_start, (torch.int32,), (p.n_heads, S), "seg_start"),
+        _ptr(seg_quota, (torch.int32,), (p.n_heads, S), "seg_quota"),
+        _ptr(n_seg, (torch.int32,), (p.n_heads,), "n_seg"),
+        _ptr(kept, (torch.int32,), (p.n_heads, p.budget), "kept"), ws.data_ptr(), ws.numel(),
+        _stream(stream))
+    _check(rc, "kvc_select")
+    return kept
+
+
+def gather_compact(p: Params, kept, k, v, credit_upd=None, k_out=None, v_out=None,
+                   credit_out=None, stream=None):
+    """Step 5.  Returns (k_out, v_out, credit_out)."""
+    dev = _device(kept)
+    shp = (p.n_heads, p.budget, p.head_dim)
+    if k_out is None:
+        k_out = torch.empty(shp, dtype=k.dtype, device=dev)
+    if v_out is None:
+        v_out = torch.empty(shp, dtype=v.dtype, device=dev)
+    if credit_upd is not None and credit_out is None:
+        credit_out = torch.empty((p.n_heads, p.budget), dtype=torch.int64, device=dev)
+    c = p.to_c()
+    rc = lib().kvc_gather_compact(
+        ctypes.byref(c), _ptr(kept, (torch.int32,), (p.n_heads, p.budget), "kept"),
+        _ptr(k, _BF16_LIKE, (p.n_heads, p.stride, p.head_dim), "k"),
+        _ptr(v, _BF16_LIKE, (p.n_heads, p.stride, p.head_dim), "v"),
+        _ptr(credit_upd, (torch.int64,), (p.n_heads, p.T), "credit_upd"),
+        _ptr(k_out, _BF16_LIKE, shp, "k_out"), _ptr(v_out, _BF16_LIKE, shp, "v_out"),
+        _ptr(credit_out, (torch.int64,), (p.n_heads, p.budget), "credit_out"), _stream(stream))
+    _check(rc, "kvc_gather_compact")
+    return k_out, v_out, credit_out
+
+
+def compress_event(p: Params, q, k, v, credit_in=None, ws=None, out=None, want_u=False,
+                   stream=None):
+    """The whole event.  Returns dict(k_out, v_out, credit_out, kept, u, status)."""
+    dev = _device(q, k, v)
+    shp = (p.n_heads, p.budget, p.head_dim)
+    o = dict(out or {})
+    o.setdefault("k_out", torch.empty(shp, dtype=k.dtype, device=dev))
+    o.setdefault("v_out", torch.empty(shp, dtype=v.dtype, device=dev))
+    o.setdefault("kept", torch.empty((p.n_heads, p.budget), dtype=torch.int32, device=dev))
+    if p.ema:
+        o.setdefault("credit_out", torch.empty((p.n_heads, p.budget), dtype=torch.int64, device=dev))
+    if want_u:
+        o.setdefault("u", torch.empty((p.n_heads, p.T), dtype=torch.float32, device=dev))
+    ws = _ws(p, ws, dev)
+    c = p.to_c()
+    rc = lib().kvc_compress_event(
+        ctypes.byref(c),
+        _ptr(q, _BF16_LIKE, (p.n_heads, p.group, p.window, p.head_dim), "q_win"),
+        _ptr(k, _BF16_LIKE, (p.n_heads, p.stride, p.head_dim), "k"),
+        _ptr(v, _BF16_LIKE, (p.n_heads, p.stride, p.head_dim), "v"),
+        _ptr(credit_in, (torch.int64,), (p.n_heads, p.n_prev), "credit_in"),
+        _ptr(o["k_out"], _BF16_LIKE, shp, "k_out"), _ptr(o["v_out"], _BF16_LIKE, shp, "v_out"),
+        _ptr(o.get("credit_out"), (torch.int64,), (p.n_heads, p.budget), "credit_out"),
+        _ptr(o["kept"], (torch.int32,), (p.n_heads, p.budget), "kept"),
+        _ptr(o.get("u"), (torch.float32,), (p.n_heads, p.T), "u_out"), ws.data_ptr(),
+        ws.numel(), _stream(stream))
+    o["status"] = _check(rc, "kvc_compress_event")
+    return o

@@ -1,0 +1,195 @@
+/*
+ * kvc.h -- C ABI of libkvc: the decode-time KV-cache compression event
+ * (adaptive mass-segmented selection) on AMD MI355X (gfx950).
+ *
+ * Sources.  The operation is the event described in the notes on
+ * "Adaptive Mass-Segmented KV Compression for Long-Form Reasoning" (AMS):
+ * section 整体框架 (overall framework) says selection runs independently for
+ * every layer and KV head on the current cache and yields a compact cache of
+ * the target budget; 关键设计 1-4 (key designs 1-4) give the mass, the
+ * cumulative-mass cuts, the segment quotas and the in-segment selection with
+ * gather-and-compact.  The one-segment special case is the max-pooled global
+ * top-K of the notes on "RefreshKV: Updating Small KV Cache During Long-form
+ * Generation" (A2 method details, prefill stage; A6 appendix, baselines).
+ *
+ * Conventions shared by every entry point.
+ *  - One call covers n_heads independent head-events (layer x batch x KV
+ *    head).  Head n's data is the n-th slab of every array.
+ *  - Every pointer except `params` and the returned strings is a DEVICE
+ *    pointer owned by the caller.  The library allocates no memory, keeps no
+ *    state between calls and never synchronises: all work is enqueued on
+ *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and
+ *    completes asynchronously.  Results are deterministic: the same inputs
+ *    give the same bits on every run.
+ *  - All arguments are validated on the host before anything is enqueued; on
+ *    an error return nothing has been launched and no output was touched.
+ *  - Return values: KVC_OK (0), KVC_NOOP (1, informational: T <= budget, so
+ *    nothing is evicted), negative = error (see kvc_strerror).
+ *  - bf16 tensors are raw IEEE bfloat16; q, k, v, k_out, v_out must be
+ *    16-byte aligned; fp32/u64/i32 arrays need their natural alignment.
+ *  - Outputs may not overlap inputs (KVC_EINVAL).
+ *  - Calls that share a workspace or outputs must be ordered on one stream.
+ *  - Precondition (not checked): q and k are finite.
+ *
+ * Array layouts (row-major, innermost last; NH = n_heads, G = group,
+ * W = window, d = head_dim, S = kvc_segment_capacity(p)):
+ *   q_win      bf16 [NH][G][W][d]     last W queries of the G query heads
+ *                                      that share each KV head (post-RoPE);
+ *                                      window query w sits at position T-W+w
+ *   k, v       bf16 [NH][t_stride][d] cached keys/values, rows >= T unused
+ *   u          f32  [NH][T]            window usage (step 1 output)
+ *   score      f32  [NH][T]            pooled usage, the base score
+ *   credit_in  u64  [NH][n_prev]       carried EMA credit, Q44 fixed point
+ *   credit_upd u64  [NH][T]            updated credit per position, Q44
+ *   seg_start  i32  [NH][S]            first position of each segment
+ *   seg_quota  i32  [NH][S]            positions to pick in each segment
+ *   n_seg      i32  [NH]               segments used per head
+ *   kept       i32  [NH][budget]       kept positions, ascending; -1 pads the
+ *                                      tail only when T < budget
+ *   k_out,v_out bf16 [NH][budget][d]   compacted cache (zero rows past T)
+ *   credit_out u64  [NH][budget]       credit of the kept positions
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+enum kvc_status {
+  KVC_OK = 0,
+  KVC_NOOP = 1,           /* T <= budget: kept = 0..T-1, identity copy      */
+  KVC_EINVAL = -1,        /* a shape or parameter is out of range, a
+                             required pointer is NULL, or outputs alias
+                             inputs                                          */
+  KVC_EALIGN = -2,        /* a pointer is not aligned as required           */
+  KVC_EWORKSPACE = -3,    /* ws is NULL or ws_bytes < kvc_workspace_bytes() */
+  KVC_EUNSUPPORTED = -4,  /* head_dim or group outside the built variants   */
+  KVC_EDEVICE = -5        /* the HIP runtime reported a launch error        */
+};
+
+enum { KVC_POOL_AVG = 0, KVC_POOL_MAX = 1 };
+enum { KVC_AGG_SUM = 0, KVC_AGG_MAX = 1 };
+
+/* Event parameters, named after the pages' quantities.  Field order fixes the
+ * layout: 17 int32, one float, then four doubles (104 bytes, no padding). */
+typedef struct kvc_params {
+  int32_t n_heads;     /* NH independent head-events; 0 = nothing to do      */
+  int32_t group;       /* G query heads per KV head, 1..64                   */
+  int32_t head_dim;    /* d, 64 or 128                                       */
+  int32_t T;           /* valid cached positions per head, 1..2^20           */
+  int32_t t_stride;    /* rows allocated per head in k/v (>= T)              */
+  int32_t window;      /* W recent queries, 1..T, W*G <= 4096                */
+  int32_t budget;      /* K positions kept per head, >= 1                    */
+  int32_t seg_min;     /* shortest segment after merging (>= 1), e.g. 16     */
+  int32_t seg_max;     /* longest segment after splitting, e.g. 256; 0 = none*/
+  int32_t q_min;       /* per-segment minimum quota (>= 0), e.g. 1           */
+  int32_t sinks;       /* leading must-keep positions (>= 0), e.g. 4         */
+  int32_t recent;      /* trailing must-keep positions (>= 0), e.g. 64       */
+  int32_t pool_kernel; /* odd pooling width 1..63, e.g. 7                    */
+  int32_t pool_mode;   /* KVC_POOL_AVG (AMS) or KVC_POOL_MAX (SnapKV-style)  */
+  int32_t head_agg;    /* KVC_AGG_SUM or KVC_AGG_MAX over the G query heads  */
+  int32_t ema;         /* 1 = EMA credit on, 0 = off                         */
+  int32_t n_prev;      /* credit entries carried per head (0..T; 0 if !ema)  */
+  float scale;         /* softmax scale; 0 => 1/sqrt(head_dim)               */
+  double delta;        /* target segment mass Delta in (0, inf); >= 1 => no
+                          mass cuts; at most 1024 thresholds                 */
+  double lambda;       /* EMA decay, [0,1], e.g. 0.9                          */
+  double beta;         /* weight of the current mass, [0,1], e.g. 0.9        */
+  double eps;          /* mass floor epsilon, (0, 1], e.g. 1e-6              */
+} kvc_params;
+
+/* Step 1: window score [AMS notes, key design 1: usage of the most recent W
+ * queries per cached position, partly observed suffix filled with the window
+ * maximum; SkipKV notes §4.1: softmax(QK^T/sqrt(d)) over an observation window
+ * with GQA head mapping].
+ * u[n][t] = AGG_g sum_{w : T-W+w >= t} softmax_t'(scale*<q[n][g][w], k[n][t']>)
+ * over t' <= T-W+w (AGG = sum or max over g of the per-head sums), then
+ * u[n][t] = max_{t' <= T-W} u[n][t'] for t > T-W.  fp32 output; bf16 matrix
+ * products with fp32 accumulation, fp32 softmax.
+ * ws: at least kvc_workspace_bytes(p). */
+int kvc_score_window(const kvc_params* p, const void* q_win, const void* k, float* u,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Step 2 + step 3: mass, prefix and segmentation with quotas [AMS notes, key
+ * design 1 (mass eq. m_i = (max(u_i,0)+eps)/sum, EMA eq.), key design 2 (C(t),
+ * b_k = min{t : C(t) >= k*Delta}, split/merge to seg_min/seg_max), key
+ * design 3 (must-keep sinks + recent suffix, q_i^min = min(q_min, L_i),
+ * remainder split by segment mass with rounding, clip and redistribute)].
+ * score[n][t] = pooled u (avg or max over pool_kernel in-range neighbours).
+ * With ema: credit_in (may be NULL only when n_prev == 0) is the carried
+ * credit of positions 0..n_prev-1; credit_upd receives the updated credit of
+ * every position (required when ema, ignored otherwise).
+ * Outputs seg_start/seg_quota/n_seg as laid out above.  Integer decisions
+ * follow an exact fixed-point contract, bit-identical to a sequential
+ * evaluation.  Returns KVC_NOOP (n_seg = 0) when T <= budget. */
+int kvc_mass_segment(const kvc_params* p, const float* u, const uint64_t* credit_in,
+                     float* score, uint64_t* credit_upd, int32_t* seg_start,
+                     int32_t* seg_quota, int32_t* n_seg, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Step 4: select [AMS notes, key design 3, last paragraph: union with the
+ * must-keep set counting duplicates once, over budget drop low-score picks,
+ * under budget add high-score unselected positions; key design 4: per-segment
+ * top-k on a base score of shape [B,Hkv,T], kept indices sorted].
+ * score: any finite fp32 base score (the pooled usage by default).  In each
+ * segment the min(quota, candidates) non-must-keep positions with the largest
+ * score are picked, ties to the lower position; the result always holds
+ * min(budget, T) positions in ascending order.  Returns KVC_NOOP (kept =
+ * 0..T-1, -1 padded) when T <= budget. */
+int kvc_select(const kvc_params* p, const float* score, const int32_t* seg_start,
+               const int32_t* seg_quota, const int32_t* n_seg, int32_t* kept, void* ws,
+               size_t ws_bytes, void* stream);
+
+/* Step 5: gather-and-compact [AMS notes, key design 4: the same kept indices
+ * gather K and V into a fixed-length per-head cache; key design 1, last
+ * paragraph: the credit follows the kept positions].
+ * k_out[n][j] = k[n][kept[n][j]], v_out likewise, credit_out[n][j] =
+ * credit_upd[n][kept[n][j]] (both credit pointers NULL, or both set); rows
+ * with kept = -1 are zero-filled.  Bitwise copies; no workspace. */
+int kvc_gather_compact(const kvc_params* p, const int32_t* kept, const void* k, const void* v,
+                       const uint64_t* credit_upd, void* k_out, void* v_out,
+                       uint64_t* credit_out, void* stream);
+
+/* The whole event, steps 1-5 in one enqueue [AMS notes, overall framework].
+ * credit_in/credit_out as above (credit_out required when ema); u_out (may be
+ * NULL) receives the step-1 usage.  kept_out receives the kept positions.
+ * Equals kvc_score_window -> kvc_mass_segment -> kvc_select ->
+ * kvc_gather_compact on the same arguments, bit for bit.
+ * The caller keeps counting logical (RoPE) positions from its generation
+ * count; the compacted cache changes only the physical slots [AMS notes,
+ * key design 4, appendix E paragraph]. */
+int kvc_compress_event(const kvc_params* p, const void* q_win, const void* k, const void* v,
+                       const uint64_t* credit_in, void* k_out, void* v_out,
+                       uint64_t* credit_out, int32_t* kept_out, float* u_out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Workspace bytes any entry point above needs for these parameters (0 when
+ * the parameters are invalid).  Pure host function. */
+size_t kvc_workspace_bytes(const kvc_params* p);
+
+/* Segment capacity S per head: n_thr + 1 + floor(T/seg_max) capped at T,
+ * with n_thr = #{k >= 1 : k*delta < 1}; seg_max = 0 drops the second term.
+ * Returns a negative status for invalid parameters.  Pure host function. */
+int kvc_segment_capacity(const kvc_params* p);
+
+/* Validates the parameters alone (no pointers): KVC_OK or the error code.
+ * Pure host function. */
+int kvc_check_params(const kvc_params* p);
+
+/* Static description of a status code. */
+const char* kvc_strerror(int status);
+
+/* KVC_ABI_VERSION of the built library. */
+int kvc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,177 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/kvc.h declares, and its host-side validation (pure host code that
+returns before anything is launched) behaves as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from eviction_window_qk_amd import kvc
+from eviction_window_qk_amd import build as kbuild
+from oracle import ams
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kvc.LIB_PATH),
+                                reason="libkvc.so not built (python -m eviction_window_qk_amd.build)")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**\s*(kvc_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for fn in ["kvc_score_window", "kvc_mass_segment", "kvc_select", "kvc_gather_compact",
+               "kvc_compress_event"]:
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported():
+    exported = kbuild.exported_symbols(kvc.LIB_PATH)
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    L = kvc.lib()
+    for n in _declared():
+        assert hasattr(L, n)
+
+
+def test_abi_version_and_strerror():
+    assert kvc.abi_version() == 1
+    for code in (0, 1, -1, -2, -3, -4, -5):
+        assert kvc.strerror(code) and kvc.strerror(code) != "unknown status"
+    assert kvc.strerror(-99) == "unknown status"
+
+
+def test_param_struct_layout():
+    assert ctypes.sizeof(kvc._CParams) == 104
+    assert kvc._CParams.delta.offset == 72
+
+
+def _p(**kw):
+    base = dict(n_heads=4, T=768, window=128, budget=256, group=7, head_dim=128)
+    base.update(kw)
+    return kvc.Params(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), -4), (dict(group=65), -4), (dict(group=0), -1),
+    (dict(T=0), -1), (dict(T=(1 << 18) + 1), -1), (dict(t_stride=100), -1),
+    (dict(window=0), -1), (dict(window=769), -1), (dict(budget=0), -1),
+    (dict(delta=0.0), -1), (dict(delta=-1.0), -1), (dict(delta=float("nan")), -1),
+    (dict(delta=1e-4), -1),                  # > 1024 thresholds
+    (dict(seg_min=0), -1), (dict(seg_max=-1), -1), (dict(q_min=-1), -1),
+    (dict(sinks=-1), -1), (dict(recent=-1), -1), (dict(pool_kernel=6), -1),
+    (dict(pool_kernel=65), -1), (dict(pool_mode=2), -1), (dict(head_agg=3), -1),
+    (dict(lam=1.5), -1), (dict(beta=-0.1), -1), (dict(eps=0.0), -1), (dict(eps=2.0), -1),
+    (dict(n_prev=5), -1),                    # credit without EMA
+    (dict(ema=True, n_prev=769), -1), (dict(scale=-1.0), -1),
+    (dict(window=128, group=64), -1),        # W*G > 4096
+    (dict(T=2048, window=512, group=8), -1), # W*G = 4096 but 7*W*W*G >= 2^22
+    (dict(n_heads=-1), -1),
+])
+def test_invalid_params(kw, code):
+    p = _p(**kw)
+    assert kvc.check_params(p) == code
+    assert kvc.workspace_bytes(p) == 0
+
+
+def test_valid_params_for_every_workload():
+    from eviction_window_qk_amd import synth
+    for name in synth.ORDER:
+        wl = synth.WORKLOADS[name]
+        p = kvc.Params.from_dict(wl.event_params(), n_heads=wl.n_heads,
+                                 n_prev=wl.budget if wl.params.get("ema") else 0)
+        assert kvc.check_params(p) == 0, name
+        assert kvc.workspace_bytes(p) > 0
+
+
+def test_segment_capacity_matches_oracle_bound():
+    for kw in [dict(), dict(seg_max=0), dict(delta=0.25), dict(delta=1.0, seg_max=0),
+               dict(T=131072, window=128, group=4, budget=4096), dict(T=20, window=4, budget=5,
+                                                                    seg_max=2, delta=0.05)]:
+        p = _p(**kw)
+        o = ams.Params(T=p.T, window=p.window, budget=p.budget, delta=p.delta, seg_min=p.seg_min,
+                       seg_max=p.seg_max)
+        assert kvc.segment_capacity(p) == ams.segment_capacity(o)
+    assert kvc.segment_capacity(_p(T=131072, window=128, group=4, budget=4096)) == 522
+
+
+def test_workspace_grows_with_heads():
+    assert kvc.workspace_bytes(_p(n_heads=8)) > kvc.workspace_bytes(_p(n_heads=4)) > 0
+
+
+# --- pointer validation: returns before any launch ---------------------------
+
+FAKE = 1 << 40          # aligned, never dereferenced
+
+
+def _call_score(p, q=FAKE, k=FAKE + (1 << 32), u=FAKE + (2 << 32), ws=FAKE + (3 << 32), wsb=None):
+    c = p.to_c()
+    if wsb is None:
+        wsb = kvc.workspace_bytes(p)
+    return kvc.lib().kvc_score_window(ctypes.byref(c), q, k, u, ws, wsb, None)
+
+
+def test_null_pointers_rejected():
+    p = _p()
+    assert _call_score(p, q=None) == -1
+    assert _call_score(p, u=None) == -1
+
+
+def test_misaligned_rejected():
+    assert _call_score(_p(), q=FAKE + 2) == -2
+
+
+def test_small_workspace_rejected():
+    p = _p()
+    assert _call_score(p, wsb=kvc.workspace_bytes(p) - 1) == -3
+    assert _call_score(p, ws=None) == -3
+
+
+def test_aliasing_rejected():
+    assert _call_score(_p(), u=FAKE + 64) == -1          # u overlaps q
+
+
+def test_zero_heads_is_a_noop_without_pointers():
+    p = _p(n_heads=0)
+    c = p.to_c()
+    assert kvc.lib().kvc_score_window(ctypes.byref(c), None, None, None, None, 0, None) == 0
+    assert kvc.lib().kvc_compress_event(ctypes.byref(c), None, None, None, None, None, None, None,
+                                        None, None, None, 0, None) == 0
+
+
+def test_gather_credit_pointers_both_or_neither():
+    p = _p()
+    c = p.to_c()
+    L = kvc.lib()
+    a = FAKE
+    rc = L.kvc_gather_compact(ctypes.byref(c), a, a + (1 << 32), a + (2 << 32), a + (3 << 32),
+                              a + (4 << 32), a + (5 << 32), None, None)
+    assert rc == -1
+
+
+def test_event_rejects_missing_credit_when_ema():
+    p = _p(ema=True, n_prev=256)
+    c = p.to_c()
+    a = FAKE
+    L = kvc.lib()
+    ws = kvc.workspace_bytes(p)
+    # credit_in NULL with n_prev > 0
+    rc = L.kvc_compress_event(ctypes.byref(c), a, a + (1 << 32), a + (2 << 32), None,
+                              a + (4 << 32), a + (5 << 32), a + (6 << 32), a + (7 << 32), None,
+                              a + (8 << 32), ws, None)
+    assert rc == -1
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    p = _p(n_heads=1)
+    q = torch.zeros((1, 7, 128, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 768, 128), dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError)):
+        kvc.score_window(p, q, k, u=torch.zeros((1, 768)), ws=torch.zeros(8, dtype=torch.uint8))
