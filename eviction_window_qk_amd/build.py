@@ -30,7 +30,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", I
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = {
     "kvc_host.cpp": [],
-    "kvc_score.hip": [],
+    "kvc_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],  # MFMA accumulators in VGPRs: no copies for the softmax VALU work
     "kvc_mass.hip": ["-ffp-contract=off"],
     "kvc_select.hip": [],
     "kvc_gather.hip": [],

@@ -20,7 +20,7 @@ WsLayout workspace_layout(const Derived& d) {
     off = align256(off + bytes);
     return at;
   };
-  L.stats = take(nh * size_t(d.n_chunks) * size_t(d.R) * 2 * sizeof(float));
+  L.stats = take(nh * size_t(d.R) * sizeof(float));  // row normalisers
   L.u = take(nh * T * sizeof(float));
   L.score = take(nh * T * sizeof(float));
   L.cupd = take(d.ema ? nh * T * sizeof(uint64_t) : 0);
@@ -58,6 +58,8 @@ static int derive(const kvc_params* p, Derived* d) {
   if (p->window < 1 || p->window > p->T) return KVC_EINVAL;
   const int64_t rows = int64_t(p->window) * p->group;
   if (rows > kMaxRows) return KVC_EINVAL;
+  // Row slots padded per query head to whole 32-row MFMA blocks.
+  if (int64_t(p->group) * ((p->window + 31) / 32) * 32 > kMaxRows) return KVC_EINVAL;
   // Fixed-point totals stay below 2^63: sum(ubar) <= 7*W*W*G.
   if (7 * int64_t(p->window) * p->window * p->group >= (int64_t(1) << 22)) return KVC_EINVAL;
   if (p->budget < 1) return KVC_EINVAL;
@@ -88,7 +90,6 @@ static int derive(const kvc_params* p, Derived* d) {
   d->W = p->window;
   d->K = p->budget;
   d->R = int(rows);
-  d->n_chunks = (p->T + kScoreChunk - 1) / kScoreChunk;
   d->seg_min = p->seg_min;
   d->seg_max = p->seg_max;
   d->q_min = p->q_min;

@@ -11,17 +11,14 @@ namespace kvc {
 
 constexpr int kUsageShift = 40;        // usage fixed point: trunc(ubar * 2^40)
 constexpr int kCreditShift = 44;       // credit and mixed-mass fixed point (Q44)
-constexpr int kMaxRows = 4096;         // W * G
+constexpr int kMaxRows = 4096;         // W * G, and G * ceil(W/32) * 32
 constexpr int kMaxT = 1 << 18;         // keep-mask bitmap fits one workgroup's LDS
 constexpr int kMaxThresholds = 1024;   // mass cuts per head
 constexpr int kScoreKeysPerWave = 64;  // two 32-key MFMA blocks per wave
-constexpr int kScoreWaves = 4;
-constexpr int kScoreChunk = kScoreKeysPerWave * kScoreWaves;  // keys per workgroup
 
 // Parameters after validation, with every derived quantity the kernels need.
 struct Derived {
   int NH, G, D, T, TS, W, K, R;
-  int n_chunks;                 // score key chunks per head
   int seg_min, seg_max, q_min;
   int s_keep, r_keep, t_keep;   // S', R', budget left after must-keep
   int pool_h, pool_mode, head_agg, ema, n_prev;

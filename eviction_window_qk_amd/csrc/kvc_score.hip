@@ -7,23 +7,36 @@
 // (softmax(QK^T/sqrt(d)) over an observation window, GQA map g(i) =
 // floor(i/n)); RefreshKV notes, A6 (max over the query heads of a group).
 //
-// The softmax needs each row's max and sum before any column sum can be
-// formed, so the score runs in two passes over the keys (the rows are too
-// many and too long to keep the score matrix):
-//   pass 1 (k_rowstats)  per key chunk, each row's max m and sum l of
-//                        2^(x - m), x = <q,k> * scale * log2(e);
-//   pass 2 (k_colsum)    merge the chunk statistics per row into
-//                        b = m + log2(l) and sum p = 2^(x - b) down the rows
-//                        of every key, per query head, then SUM or MAX over
-//                        the heads;
-//   fill   (k_fill)      replace the partly observed tail by the maximum over
-//                        fully observed positions.
-// Both passes keep a 64-key slab resident in registers per wave (the MFMA A
-// operand in pass 1, B in pass 2) and stream 32-row Q blocks through LDS.  In
-// pass 1 the accumulator puts one row in each lane (row stats are lane-local
-// plus one cross-half exchange); in pass 2 it puts one key in each lane
-// (column sums are lane-local plus one cross-half exchange).  No atomics:
-// every sum has a fixed order, so u is bitwise reproducible.
+// A column sum of softmax probabilities needs every row's max and sum first,
+// and the score matrix (W*G rows x T keys per head) is far too large to keep,
+// so the score runs in two passes over the keys, each a bf16 MFMA
+// (32x32x16, fp32 accumulate) stream:
+//
+//   k_rowstats  rows stationary: each wave keeps 64 query rows in registers
+//               (the B operand) and the workgroup streams every key of the
+//               head through double-buffered LDS tiles.  The accumulator gives
+//               each lane one row and 16 keys, so the running max m and sum l
+//               of 2^(x-m), x = <q,k>*scale*log2(e), stay lane-local; the two
+//               lane halves merge once at the end.  Output: the row
+//               normaliser b = m + log2(l) (log2 domain).
+//   k_colsum    keys stationary: each wave keeps 64 keys in registers (the B
+//               operand) and the workgroup streams the query rows through
+//               double-buffered LDS.  The accumulator gives each lane one key
+//               and 16 rows, so p = 2^(x - b) summed down the rows is
+//               lane-local; the halves merge at the end (per query head for
+//               the MAX aggregation).
+//   k_fill      positions seen by fewer than W queries take the maximum over
+//               the fully observed ones.
+//
+// Per score element the VALU work is one FMA, one exp2 and one add (plus half
+// a max in pass 1).  Both passes are software-pipelined: the MFMAs of one
+// 32-wide block are issued interleaved with the softmax arithmetic of the
+// previous block, so the matrix cores and the vector ALUs of a SIMD work at
+// the same time even within one wave.  The causal mask costs nothing on
+// blocks every row sees fully; only blocks reaching past T-W take the masked
+// loop.  No atomics: every sum has a fixed order, so u is bitwise
+// reproducible.  Blocks are renumbered so that the workgroups of one head
+// share an XCD and its L2.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -31,10 +44,15 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRowBlock = 32;
-constexpr int kThreads = 64 * kScoreWaves;
+constexpr int kXcds = 8;
+
+// sched_group_barrier masks
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -43,195 +61,417 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Lane (j = lane & 31, h = lane >> 5) holds operand row/column j and, for
-// k-step s, head-dim elements [h*D/2 + 8s, h*D/2 + 8s + 8).  Any bijection of
-// the head dimension gives the same dot product as long as both operands use
-// it; this one makes each lane's share of a row one contiguous D-byte run.
+// Hardware dispatches block b to XCD b % 8.  Renumber so that each XCD runs a
+// contiguous range of logical blocks.
+__device__ __forceinline__ unsigned xcd_logical_block() {
+  const unsigned nb = gridDim.x, b = blockIdx.x;
+  const unsigned q = nb / kXcds, r = nb % kXcds;
+  const unsigned x = b % kXcds, slot = b / kXcds;
+  return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+}
+
+// Operand layout.  Lane (j = lane & 31, h = lane >> 5) supplies row/column j
+// of a 32-wide MFMA operand and, for k-step s, head-dim elements
+// [h*D/2 + 8s, h*D/2 + 8s + 8).  Any bijection of the head dimension gives the
+// same dot product as long as both operands use it; this one makes a lane's
+// share of a row one contiguous run.  Accumulator element r of a 32x32 tile
+// is at (row 8(r/4) + 4h + (r%4), column j).
 template <int D>
-__device__ __forceinline__ void load_key_slab(const u32x4* __restrict__ kn, int T, int key_base,
-                                              int lane, u32x4 (&op)[2][D / 16]) {
+__device__ __forceinline__ void load_rows_op(const u32x4* __restrict__ base, int row, int h,
+                                             u32x4 (&op)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) op[s] = base[size_t(row) * (D / 8) + h * (D / 16) + s];
+}
+
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// ---------------------------------------------------------------------------
+// pass 1: row statistics
+// ---------------------------------------------------------------------------
+constexpr int kRsWaves = 4;
+constexpr int kRsRowBlocks = 2;                         // 32-row blocks per wave
+constexpr int kRsRows = kRsWaves * kRsRowBlocks * 32;   // rows per workgroup (256)
+constexpr int kRsTile = 64;                             // keys per LDS tile (two 32-key blocks)
+constexpr int kRsThreads = 64 * kRsWaves;
+
+// Online max/sum update of one row (this lane's) with 16 new raw dot products.
+template <bool MASK>
+__device__ __forceinline__ void row_update(f32x16 acc, float c, int t0, int h, int lim, float& m,
+                                           float& l) {
+  if (MASK) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (t0 + acc_row(r, h) > lim) acc[r] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+  mx = fmaxf(mx, acc[15]);
+  const float mn = fmaxf(m, mx);
+  // mn is -inf only while every key seen so far is masked (then l stays 0).
+  const float nb = mn == -INFINITY ? 0.0f : -mn * c;
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    s0 += fast_exp2(__builtin_fmaf(acc[r], c, nb));
+    s1 += fast_exp2(__builtin_fmaf(acc[r + 1], c, nb));
+  }
+  const float scale = m == -INFINITY ? 0.0f : fast_exp2(__builtin_fmaf(m, c, nb));
+  l = __builtin_fmaf(l, scale, s0 + s1);
+  m = mn;
+}
+
+template <int D>
+struct RsCtx {
+  u32x4 qop[kRsRowBlocks][D / 16];
+  float m[kRsRowBlocks], l[kRsRowBlocks];
+  int lim[kRsRowBlocks];
+};
+
+// MFMAs of one 32-key block (buf rows kb*32..kb*32+31) into acc, interleaved
+// with the softmax of the previous block (pacc, keys from pt0).
+template <int D, bool MASK>
+__device__ __forceinline__ void rs_step(RsCtx<D>& cx, const u32x4* __restrict__ buf, int kb,
+                                        f32x16 (&acc)[kRsRowBlocks],
+                                        const f32x16 (&pacc)[kRsRowBlocks], int pt0, float c, int j,
+                                        int h) {
+  constexpr int kStride = D / 8 + 1;
+#pragma unroll
+  for (int rb = 0; rb < kRsRowBlocks; ++rb) acc[rb] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const u32x4 a = buf[(kb * 32 + j) * kStride + h * (D / 16) + s];
+#pragma unroll
+    for (int rb = 0; rb < kRsRowBlocks; ++rb) acc[rb] = mfma32(a, cx.qop[rb][s], acc[rb]);
+  }
+#pragma unroll
+  for (int rb = 0; rb < kRsRowBlocks; ++rb)
+    row_update<MASK>(pacc[rb], c, pt0, h, cx.lim[rb], cx.m[rb], cx.l[rb]);
+  // Interleave: LDS reads one k-step ahead, two MFMAs and ~14 VALU per step.
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kRsRowBlocks, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 14, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kRsThreads, 2) void k_rowstats(Derived P, const u32x4* __restrict__ q,
+                                                            const u32x4* __restrict__ k,
+                                                            float* __restrict__ rowb) {
+  constexpr int kPerRow = D / 8;        // u32x4 per row
+  constexpr int kStride = kPerRow + 1;  // LDS row stride (one pad piece)
+  constexpr int kLoads = kRsTile * kPerRow / kRsThreads;
+  __shared__ u32x4 ks[2][kRsTile * kStride];
+
+  const int groups = (P.R + kRsRows - 1) / kRsRows;
+  const unsigned lb = xcd_logical_block();
+  const int n = lb / groups, grp = lb % groups;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, h = lane >> 5;
+  const int T = P.T, W = P.W, R = P.R;
+  const float c = P.c_log2;
+
+  RsCtx<D> cx;
+  const int row0 = grp * kRsRows + wave * (kRsRowBlocks * 32);
+  const bool wave_active = row0 < R;  // uniform per wave
+#pragma unroll
+  for (int rb = 0; rb < kRsRowBlocks; ++rb) {
+    const int r = row0 + rb * 32 + j;
+    const int rc = r < R ? r : R - 1;  // padding rows duplicate a real row, never written
+    cx.lim[rb] = T - W + rc % W;
+    load_rows_op<D>(q + size_t(n) * R * kPerRow, rc, h, cx.qop[rb]);
+    cx.m[rb] = -INFINITY;
+    cx.l[rb] = 0.0f;
+  }
+
+  const u32x4* kn = k + size_t(n) * P.TS * kPerRow;
+  const int n_tiles = (T + kRsTile - 1) / kRsTile;
+  // Tiles whose every key is seen by every row (t <= T-W) need no mask.
+  const int n_full = (T - W + 1) / kRsTile;
+  auto fetch = [&](int kt, u32x4 (&pre)[kLoads]) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int e = threadIdx.x + i * kRsThreads;
+      int t = kt * kRsTile + e / kPerRow;
+      t = t < T ? t : T - 1;  // rows past T are masked; keep the load in bounds
+      pre[i] = kn[size_t(t) * kPerRow + e % kPerRow];
+    }
+  };
+  auto stash = [&](int buf, const u32x4 (&pre)[kLoads]) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int e = threadIdx.x + i * kRsThreads;
+      ks[buf][(e / kPerRow) * kStride + e % kPerRow] = pre[i];
+    }
+  };
+
+  u32x4 pre[kLoads];
+  fetch(0, pre);
+  stash(0, pre);
+  if (n_tiles > 1) fetch(1, pre);
+  __syncthreads();
+
+  // accB starts as a pending block of -inf: its update leaves (m, l) unchanged.
+  f32x16 accA[kRsRowBlocks], accB[kRsRowBlocks];
+#pragma unroll
+  for (int rb = 0; rb < kRsRowBlocks; ++rb) {
+    accA[rb] = f32x16{};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accB[rb][r] = -INFINITY;
+  }
+  int kt = 0;
+  // Unmasked tiles: two 32-key blocks each, pipelined across blocks and tiles.
+  for (; kt < n_full; ++kt) {
+    const u32x4* buf = ks[kt & 1];
+    if (wave_active) {
+      rs_step<D, false>(cx, buf, 0, accA, accB, kt * kRsTile - 32, c, j, h);
+      rs_step<D, false>(cx, buf, 1, accB, accA, kt * kRsTile, c, j, h);
+    }
+    // Unconditional (past the end: a clamped reload into the idle buffer) so
+    // the loop body stays one basic block for the MFMA/VALU interleave.
+    stash((kt + 1) & 1, pre);
+    fetch(kt + 2, pre);
+    __syncthreads();
+  }
+  // Tiles that reach past T-W: same pipeline with the causal mask.
+  for (; kt < n_tiles; ++kt) {
+    const u32x4* buf = ks[kt & 1];
+    if (wave_active) {
+      rs_step<D, true>(cx, buf, 0, accA, accB, kt * kRsTile - 32, c, j, h);
+      rs_step<D, true>(cx, buf, 1, accB, accA, kt * kRsTile, c, j, h);
+    }
+    // Unconditional (past the end: a clamped reload into the idle buffer) so
+    // the loop body stays one basic block for the MFMA/VALU interleave.
+    stash((kt + 1) & 1, pre);
+    fetch(kt + 2, pre);
+    __syncthreads();
+  }
+  if (!wave_active) return;
+  // Last block still pending in accB (keys from (n_tiles-1)*64 + 32).
+#pragma unroll
+  for (int rb = 0; rb < kRsRowBlocks; ++rb)
+    row_update<true>(accB[rb], c, (n_tiles - 1) * kRsTile + 32, h, cx.lim[rb], cx.m[rb], cx.l[rb]);
+
+  // Merge the two lane halves (same row, different keys) and write b.
+#pragma unroll
+  for (int rb = 0; rb < kRsRowBlocks; ++rb) {
+    const float mo = __shfl_xor(cx.m[rb], 32);
+    const float lo = __shfl_xor(cx.l[rb], 32);
+    const float mm = fmaxf(cx.m[rb], mo);
+    float ll = 0.0f;
+    if (cx.m[rb] != -INFINITY) ll += cx.l[rb] * fast_exp2((cx.m[rb] - mm) * c);
+    if (mo != -INFINITY) ll += lo * fast_exp2((mo - mm) * c);
+    const int r = row0 + rb * 32 + j;
+    if (h == 0 && r < R) rowb[size_t(n) * R + r] = mm * c + __log2f(ll);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pass 2: column sums
+// ---------------------------------------------------------------------------
+constexpr int kCsWaves = 4;
+constexpr int kCsKeys = kCsWaves * kScoreKeysPerWave;  // keys per workgroup (256)
+constexpr int kCsBatch = 2;                            // 32-row blocks per LDS buffer
+constexpr int kCsThreads = 64 * kCsWaves;
+
+template <int D>
+struct CsCtx {
+  u32x4 kop[2][D / 16];
+  float cs0, cs1;
+  int key0;  // this lane's first key (second is key0 + 32)
+};
+
+// Column sums of one 32-row block's probabilities (accumulators a0/a1, row
+// normalisers bblk[0..32) in LDS).
+template <bool MASK>
+__device__ __forceinline__ void col_update(const f32x16& a0, const f32x16& a1,
+                                           const float* __restrict__ bblk, float c, int T, int W,
+                                           int wbase, int key0, int h, float& cs0, float& cs1) {
+  float b[16];
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) {
+    const f32x4 bb = *reinterpret_cast<const f32x4*>(&bblk[8 * i4 + 4 * h]);
+    b[4 * i4 + 0] = bb[0];
+    b[4 * i4 + 1] = bb[1];
+    b[4 * i4 + 2] = bb[2];
+    b[4 * i4 + 3] = bb[3];
+  }
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x0 = __builtin_fmaf(a0[r], c, -b[r]);
+    float x1 = __builtin_fmaf(a1[r], c, -b[r]);
+    if (MASK) {
+      const int lim = T - W + wbase + acc_row(r, h);
+      x0 = key0 > lim ? -INFINITY : x0;
+      x1 = key0 + 32 > lim ? -INFINITY : x1;
+    }
+    s0 += fast_exp2(x0);
+    s1 += fast_exp2(x1);
+  }
+  cs0 += s0;
+  cs1 += s1;
+}
+
+template <int D, bool MASK>
+__device__ __forceinline__ void cs_step(CsCtx<D>& cx, const u32x4* __restrict__ buf, int bi,
+                                        f32x16& a0, f32x16& a1, const f32x16& p0,
+                                        const f32x16& p1, const float* __restrict__ pb,
+                                        int pwbase, float c, int T, int W, int j, int h) {
+  constexpr int kStride = D / 8 + 1;
+  a0 = f32x16{};
+  a1 = f32x16{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const u32x4 a = buf[(bi * 32 + j) * kStride + h * (D / 16) + s];
+    a0 = mfma32(a, cx.kop[0][s], a0);
+    a1 = mfma32(a, cx.kop[1][s], a1);
+  }
+  col_update<MASK>(p0, p1, pb, c, T, W, pwbase, cx.key0, h, cx.cs0, cx.cs1);
+  // Interleave: the normaliser reads and LDS reads one k-step ahead, then two
+  // MFMAs and ~12 VALU per step.
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 12, 0);
+  }
+}
+
+template <int D, bool MASK>
+__device__ void cs_run(CsCtx<D>& cx, u32x4 (*qs)[kCsBatch * 32 * (D / 8 + 1)],
+                       const float* __restrict__ bsh, const u32x4* __restrict__ qn, int n_blocks,
+                       int n_rb, float c, int T, int W, int j, int h) {
+  constexpr int kPerRow = D / 8;
+  constexpr int kStride = kPerRow + 1;
+  constexpr int kLoads = kCsBatch * 32 * kPerRow / kCsThreads;
+  auto fetch = [&](int batch, u32x4 (&pre)[kLoads]) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int e = threadIdx.x + i * kCsThreads;
+      int blk = batch * kCsBatch + e / (32 * kPerRow);
+      blk = blk < n_blocks ? blk : n_blocks - 1;
+      const int g = blk / n_rb;
+      int w = (blk % n_rb) * 32 + (e / kPerRow) % 32;
+      w = w < W ? w : W - 1;  // padding slots carry b = +inf, so their rows add 0
+      pre[i] = qn[size_t(g * W + w) * kPerRow + e % kPerRow];
+    }
+  };
+  auto stash = [&](int buf, const u32x4 (&pre)[kLoads]) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int e = threadIdx.x + i * kCsThreads;
+      qs[buf][(e / kPerRow) * kStride + e % kPerRow] = pre[i];
+    }
+  };
+  const int n_batches = (n_blocks + kCsBatch - 1) / kCsBatch;
+  u32x4 pre[kLoads];
+  fetch(0, pre);
+  __syncthreads();  // b table ready
+  stash(0, pre);
+  if (n_batches > 1) fetch(1, pre);
+  __syncthreads();
+
+  // (a0B, a1B) start as a pending block of -inf: its column sums add +0.0.
+  f32x16 a0A, a1A, a0B, a1B;
+  a0A = a1A = f32x16{};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a0B[r] = a1B[r] = -INFINITY;
+  const int full_batches = n_blocks / kCsBatch;
+  int bt = 0;
+  for (; bt < full_batches; ++bt) {
+    const u32x4* buf = qs[bt & 1];
+    const int blk = bt * kCsBatch;
+    cs_step<D, MASK>(cx, buf, 0, a0A, a1A, a0B, a1B, bsh + (blk > 0 ? blk - 1 : 0) * 32,
+                     ((blk - 1 + n_blocks) % n_rb) * 32, c, T, W, j, h);
+    cs_step<D, MASK>(cx, buf, 1, a0B, a1B, a0A, a1A, bsh + blk * 32, (blk % n_rb) * 32, c, T, W,
+                     j, h);
+    stash((bt + 1) & 1, pre);  // unconditional: see k_rowstats
+    fetch(bt + 2, pre);
+    __syncthreads();
+  }
+  int last = full_batches * kCsBatch - 1;  // block pending in (a0B, a1B)
+  if (bt < n_batches) {                    // odd block count: one more block
+    const u32x4* buf = qs[bt & 1];
+    const int blk = bt * kCsBatch;
+    cs_step<D, MASK>(cx, buf, 0, a0A, a1A, a0B, a1B, bsh + (blk > 0 ? blk - 1 : 0) * 32,
+                     ((blk - 1 + n_blocks) % n_rb) * 32, c, T, W, j, h);
+    col_update<MASK>(a0A, a1A, bsh + blk * 32, c, T, W, (blk % n_rb) * 32, cx.key0, h, cx.cs0,
+                     cx.cs1);
+  } else if (last >= 0) {
+    col_update<MASK>(a0B, a1B, bsh + last * 32, c, T, W, (last % n_rb) * 32, cx.key0, h, cx.cs0,
+                     cx.cs1);
+  }
+}
+
+template <int D, bool SUM>
+__global__ __launch_bounds__(kCsThreads, 2) void k_colsum(Derived P, const u32x4* __restrict__ q,
+                                                          const u32x4* __restrict__ k,
+                                                          const float* __restrict__ rowb,
+                                                          float* __restrict__ u) {
+  constexpr int kPerRow = D / 8;
+  constexpr int kStride = kPerRow + 1;
+  __shared__ u32x4 qs[2][kCsBatch * 32 * kStride];
+  __shared__ __align__(16) float bsh[kMaxRows];
+
+  const int chunks = (P.T + kCsKeys - 1) / kCsKeys;
+  const unsigned lb = xcd_logical_block();
+  const int n = lb / chunks, chunk = lb % chunks;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 31, h = lane >> 5;
+  const int T = P.T, W = P.W, R = P.R, G = P.G;
+  const float c = P.c_log2;
+  const int key_base = chunk * kCsKeys + wave * kScoreKeysPerWave;
+
+  // Row blocks enumerate (g, rb) so that no block straddles two query heads:
+  // block i covers window slots [rb*32, min(W, rb*32+32)) of head g.
+  const int n_rb = (W + 31) / 32;
+  const int n_blocks = G * n_rb;
+  for (int i = threadIdx.x; i < n_blocks * 32; i += kCsThreads) {
+    const int g = i / (n_rb * 32), w = i % (n_rb * 32);
+    bsh[i] = w < W ? rowb[size_t(n) * R + g * W + w] : INFINITY;  // +inf: p = 0
+  }
+
+  CsCtx<D> cx;
+  cx.key0 = key_base + j;
+  const u32x4* kn = k + size_t(n) * P.TS * kPerRow;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int t = key_base + kb * 32 + j;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      op[kb][s] = t < T ? kn[size_t(t) * (D / 8) + h * (D / 16) + s] : u32x4{0, 0, 0, 0};
-    }
+    int t = key_base + kb * 32 + j;
+    t = t < T ? t : T - 1;  // keys past T are never written
+    load_rows_op<D>(kn, t, h, cx.kop[kb]);
   }
-}
+  const u32x4* qn = q + size_t(n) * R * kPerRow;
 
-// Cooperative copy of window rows [w0, w0+32) of query head g into LDS
-// (row stride D/8 + 1 u32x4 to spread the banks); rows past W are zero.
-template <int D>
-__device__ __forceinline__ void stage_rows(const u32x4* __restrict__ qg, int W, int w0,
-                                           u32x4* __restrict__ qs) {
-  constexpr int kPerRow = D / 8;
-  for (int e = threadIdx.x; e < kRowBlock * kPerRow; e += kThreads) {
-    const int r = e / kPerRow, c = e % kPerRow;
-    const int w = w0 + r;
-    qs[r * (kPerRow + 1) + c] = w < W ? qg[size_t(w) * kPerRow + c] : u32x4{0, 0, 0, 0};
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void k_rowstats(Derived P, const u32x4* __restrict__ q,
-                                                       const u32x4* __restrict__ k,
-                                                       float2* __restrict__ stats) {
-  constexpr int kPerRow = D / 8;
-  __shared__ u32x4 qs[kRowBlock * (kPerRow + 1)];
-  __shared__ float2 wst[kScoreWaves][kRowBlock];
-
-  const int chunk = blockIdx.x % P.n_chunks, n = blockIdx.x / P.n_chunks;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = lane & 31, h = lane >> 5;
-  const int T = P.T, W = P.W;
-  const int key_base = chunk * kScoreChunk + wave * kScoreKeysPerWave;
-  const float c = P.c_log2;
-
-  u32x4 kop[2][D / 16];
-  load_key_slab<D>(k + size_t(n) * P.TS * kPerRow, T, key_base, lane, kop);
-
-  const int n_rb = (W + kRowBlock - 1) / kRowBlock;
-  for (int g = 0; g < P.G; ++g) {
-    const u32x4* qg = q + (size_t(n) * P.G + g) * size_t(W) * kPerRow;
-    for (int rb = 0; rb < n_rb; ++rb) {
-      __syncthreads();
-      stage_rows<D>(qg, W, rb * kRowBlock, qs);
-      __syncthreads();
-
-      f32x16 acc[2] = {};
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const u32x4 b = qs[j * (kPerRow + 1) + h * (D / 16) + s];
-        acc[0] = mfma32(kop[0][s], b, acc[0]);
-        acc[1] = mfma32(kop[1][s], b, acc[1]);
-      }
-      // acc[kb][r]: key key_base + kb*32 + 8(r/4) + 4h + (r%4), row j.
-      const int w = rb * kRowBlock + j;
-      const int lim = T - W + w;  // last key this row sees
-      float x[2][16];
-      float m = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = key_base + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          x[kb][r] = t <= lim ? acc[kb][r] * c : -INFINITY;
-          m = fmaxf(m, x[kb][r]);
-        }
-      m = fmaxf(m, __shfl_xor(m, 32));
-      float l = 0.0f;
-      if (m != -INFINITY) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) l += fast_exp2(x[kb][r] - m);
-      }
-      l += __shfl_xor(l, 32);
-      if (h == 0) wst[wave][j] = make_float2(m, l);
-      __syncthreads();
-      if (threadIdx.x < kRowBlock) {
-        const int wr = rb * kRowBlock + threadIdx.x;
-        if (wr < W) {
-          float mm = -INFINITY;
-#pragma unroll
-          for (int v = 0; v < kScoreWaves; ++v) mm = fmaxf(mm, wst[v][threadIdx.x].x);
-          float ll = 0.0f;
-          if (mm != -INFINITY) {
-#pragma unroll
-            for (int v = 0; v < kScoreWaves; ++v) {
-              const float2 st = wst[v][threadIdx.x];
-              if (st.x != -INFINITY) ll += st.y * fast_exp2(st.x - mm);
-            }
-          }
-          stats[(size_t(n) * P.n_chunks + chunk) * P.R + size_t(g) * W + wr] =
-              make_float2(mm, ll);
-        }
-      }
+  if (SUM) {
+    cx.cs0 = cx.cs1 = 0.0f;
+    // Masking is needed only when some key of this wave lies past T-W (or T).
+    const bool mask = key_base + kScoreKeysPerWave - 1 > T - W;
+    if (mask) cs_run<D, true>(cx, qs, bsh, qn, n_blocks, n_rb, c, T, W, j, h);
+    else cs_run<D, false>(cx, qs, bsh, qn, n_blocks, n_rb, c, T, W, j, h);
+    cx.cs0 += __shfl_xor(cx.cs0, 32);
+    cx.cs1 += __shfl_xor(cx.cs1, 32);
+  } else {
+    // MAX over the query heads: one head's blocks at a time.
+    float tot0 = -INFINITY, tot1 = -INFINITY;
+    for (int g = 0; g < G; ++g) {
+      cx.cs0 = cx.cs1 = 0.0f;
+      __syncthreads();  // previous head's LDS use done
+      cs_run<D, true>(cx, qs, bsh + g * n_rb * 32, qn + size_t(g) * W * kPerRow, n_rb, n_rb, c,
+                      T, W, j, h);
+      tot0 = fmaxf(tot0, cx.cs0 + __shfl_xor(cx.cs0, 32));
+      tot1 = fmaxf(tot1, cx.cs1 + __shfl_xor(cx.cs1, 32));
     }
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void k_colsum(Derived P, const u32x4* __restrict__ q,
-                                                     const u32x4* __restrict__ k,
-                                                     const float2* __restrict__ stats,
-                                                     float* __restrict__ u) {
-  constexpr int kPerRow = D / 8;
-  __shared__ u32x4 qs[kRowBlock * (kPerRow + 1)];
-  __shared__ float bsh[kMaxRows];
-
-  const int chunk = blockIdx.x % P.n_chunks, n = blockIdx.x / P.n_chunks;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = lane & 31, h = lane >> 5;
-  const int T = P.T, W = P.W;
-  const int key_base = chunk * kScoreChunk + wave * kScoreKeysPerWave;
-  const float c = P.c_log2;
-
-  // Row normaliser b_r = m_r + log2(l_r) from the per-chunk statistics,
-  // merged in chunk order.
-  const float2* sn = stats + size_t(n) * P.n_chunks * P.R;
-  for (int r = threadIdx.x; r < P.R; r += kThreads) {
-    float mm = -INFINITY;
-    for (int ch = 0; ch < P.n_chunks; ++ch) mm = fmaxf(mm, sn[size_t(ch) * P.R + r].x);
-    float ll = 0.0f;
-    for (int ch = 0; ch < P.n_chunks; ++ch) {
-      const float2 st = sn[size_t(ch) * P.R + r];
-      if (st.x != -INFINITY) ll += st.y * fast_exp2(st.x - mm);
-    }
-    bsh[r] = mm + __log2f(ll);
-  }
-
-  u32x4 kop[2][D / 16];
-  load_key_slab<D>(k + size_t(n) * P.TS * kPerRow, T, key_base, lane, kop);
-
-  float total[2];
-  total[0] = total[1] = P.head_agg == KVC_AGG_SUM ? 0.0f : -INFINITY;
-  const int n_rb = (W + kRowBlock - 1) / kRowBlock;
-  for (int g = 0; g < P.G; ++g) {
-    const u32x4* qg = q + (size_t(n) * P.G + g) * size_t(W) * kPerRow;
-    float cs[2] = {0.0f, 0.0f};
-    for (int rb = 0; rb < n_rb; ++rb) {
-      __syncthreads();
-      stage_rows<D>(qg, W, rb * kRowBlock, qs);
-      __syncthreads();
-
-      f32x16 acc[2] = {};
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const u32x4 a = qs[j * (kPerRow + 1) + h * (D / 16) + s];
-        acc[0] = mfma32(a, kop[0][s], acc[0]);
-        acc[1] = mfma32(a, kop[1][s], acc[1]);
-      }
-      // acc[kb][r]: row (window slot) rb*32 + 8(r/4) + 4h + (r%4), key
-      // key_base + kb*32 + j.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int w = rb * kRowBlock + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (w < W) {
-          const float b = bsh[g * W + w];
-          const int lim = T - W + w;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const int t = key_base + kb * 32 + j;
-            if (t <= lim) cs[kb] += fast_exp2(acc[kb][r] * c - b);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const float full = cs[kb] + __shfl_xor(cs[kb], 32);
-      total[kb] = P.head_agg == KVC_AGG_SUM ? total[kb] + full : fmaxf(total[kb], full);
-    }
+    cx.cs0 = tot0;
+    cx.cs1 = tot1;
   }
   if (h == 0) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int t = key_base + kb * 32 + j;
-      if (t < T) u[size_t(n) * T + t] = total[kb];
-    }
+    if (key_base + j < T) u[size_t(n) * T + key_base + j] = cx.cs0;
+    if (key_base + 32 + j < T) u[size_t(n) * T + key_base + 32 + j] = cx.cs1;
   }
 }
 
@@ -256,16 +496,22 @@ __global__ __launch_bounds__(256) void k_fill(Derived P, float* __restrict__ u) 
 
 hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u, float* stats,
                         hipStream_t s) {
-  const dim3 grid(unsigned(d.n_chunks) * unsigned(d.NH));
-  float2* st = reinterpret_cast<float2*>(stats);
   const u32x4* qv = static_cast<const u32x4*>(q);
   const u32x4* kv = static_cast<const u32x4*>(k);
+  const unsigned g_rs = unsigned((d.R + kRsRows - 1) / kRsRows) * unsigned(d.NH);
+  const unsigned g_cs = unsigned((d.T + kCsKeys - 1) / kCsKeys) * unsigned(d.NH);
   if (d.D == 128) {
-    k_rowstats<128><<<grid, kThreads, 0, s>>>(d, qv, kv, st);
-    k_colsum<128><<<grid, kThreads, 0, s>>>(d, qv, kv, st, u);
+    k_rowstats<128><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, stats);
+    if (d.head_agg == KVC_AGG_SUM)
+      k_colsum<128, true><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
+    else
+      k_colsum<128, false><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
   } else {
-    k_rowstats<64><<<grid, kThreads, 0, s>>>(d, qv, kv, st);
-    k_colsum<64><<<grid, kThreads, 0, s>>>(d, qv, kv, st, u);
+    k_rowstats<64><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, stats);
+    if (d.head_agg == KVC_AGG_SUM)
+      k_colsum<64, true><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
+    else
+      k_colsum<64, false><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
   }
   if (d.W > 1) k_fill<<<d.NH, 256, 0, s>>>(d, u);
   return hipGetLastError();

@@ -130,7 +130,8 @@ def test_qwen7b_ema_event_chain():
     v1 = np.zeros_like(v0)
     credit = np.zeros((len(heads), K), dtype=np.uint64)
     for i, n in enumerate(heads):
-        r0 = ams.event(widen(q0[i]), widen(k0[i]), v0[i], None, op0)
+        u0 = ams.window_usage(widen(q0[i]), widen(k0[i]), op0)
+        r0 = ams.steps2to5(u0.astype(np.float32), k0[i], v0[i], None, op0)  # bf16 bits
         fk, fv = synth.fresh_rows(wl, n, wl.T - K, seed=wl.seed)
         k1[i] = np.concatenate([r0.k_out, fk])
         v1[i] = np.concatenate([r0.v_out, fv])
