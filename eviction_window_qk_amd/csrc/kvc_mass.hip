@@ -25,7 +25,7 @@
 namespace kvc {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kScanItems = 4;
 constexpr int kMaxMerged = kMaxThresholds + 1;

@@ -128,33 +128,52 @@ struct RsCtx {
   int lim[kRsRowBlocks];
 };
 
-// MFMAs of one 32-key block (buf rows kb*32..kb*32+31) into acc, interleaved
-// with the softmax of the previous block (pacc, keys from pt0).
-template <int D, bool MASK>
-__device__ __forceinline__ void rs_step(RsCtx<D>& cx, const u32x4* __restrict__ buf, int kb,
-                                        f32x16 (&acc)[kRsRowBlocks],
-                                        const f32x16 (&pacc)[kRsRowBlocks], int pt0, float c, int j,
-                                        int h) {
+// A-operand fragments (one 32-key block) of k-steps 0..D/16-1 from LDS.
+template <int D>
+__device__ __forceinline__ void load_frags(const u32x4* __restrict__ buf, int blk, int j, int h,
+                                           u32x4 (&f)[D / 16]) {
   constexpr int kStride = D / 8 + 1;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = buf[(blk * 32 + j) * kStride + h * (D / 16) + s];
+}
+
+// MFMAs of one 32-key block (fragments already in registers) into acc,
+// interleaved with the softmax of the previous block (pacc, keys from pt0).
+template <int D, bool MASK>
+__device__ __forceinline__ void rs_step(RsCtx<D>& cx, const u32x4 (&fa)[D / 16],
+                                        f32x16 (&acc)[kRsRowBlocks],
+                                        const f32x16 (&pacc)[kRsRowBlocks], int pt0, float c,
+                                        int h) {
 #pragma unroll
   for (int rb = 0; rb < kRsRowBlocks; ++rb) acc[rb] = f32x16{};
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    const u32x4 a = buf[(kb * 32 + j) * kStride + h * (D / 16) + s];
 #pragma unroll
-    for (int rb = 0; rb < kRsRowBlocks; ++rb) acc[rb] = mfma32(a, cx.qop[rb][s], acc[rb]);
+    for (int rb = 0; rb < kRsRowBlocks; ++rb) acc[rb] = mfma32(fa[s], cx.qop[rb][s], acc[rb]);
   }
 #pragma unroll
   for (int rb = 0; rb < kRsRowBlocks; ++rb)
     row_update<MASK>(pacc[rb], c, pt0, h, cx.lim[rb], cx.m[rb], cx.l[rb]);
-  // Interleave: LDS reads one k-step ahead, two MFMAs and ~14 VALU per step.
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, kRsRowBlocks, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, 14, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 15, 0);
   }
+}
+
+// One 64-key LDS tile: both blocks' fragments are read up front, then
+// MFMA(block 0) || softmax(previous block), MFMA(block 1) || softmax(block 0).
+template <int D, bool MASK>
+__device__ __forceinline__ void rs_tile(RsCtx<D>& cx, const u32x4* __restrict__ buf,
+                                        f32x16 (&accA)[kRsRowBlocks],
+                                        f32x16 (&accB)[kRsRowBlocks], int t0, float c, int j,
+                                        int h) {
+  u32x4 f0[D / 16], f1[D / 16];
+  load_frags<D>(buf, 0, j, h, f0);
+  load_frags<D>(buf, 1, j, h, f1);
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * (D / 16), 0);
+  rs_step<D, MASK>(cx, f0, accA, accB, t0 - 32, c, h);
+  rs_step<D, MASK>(cx, f1, accB, accA, t0, c, h);
 }
 
 template <int D>
@@ -226,10 +245,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_rowstats(Derived P, const u32
   // Unmasked tiles: two 32-key blocks each, pipelined across blocks and tiles.
   for (; kt < n_full; ++kt) {
     const u32x4* buf = ks[kt & 1];
-    if (wave_active) {
-      rs_step<D, false>(cx, buf, 0, accA, accB, kt * kRsTile - 32, c, j, h);
-      rs_step<D, false>(cx, buf, 1, accB, accA, kt * kRsTile, c, j, h);
-    }
+    if (wave_active) rs_tile<D, false>(cx, buf, accA, accB, kt * kRsTile, c, j, h);
     // Unconditional (past the end: a clamped reload into the idle buffer) so
     // the loop body stays one basic block for the MFMA/VALU interleave.
     stash((kt + 1) & 1, pre);
@@ -239,10 +255,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_rowstats(Derived P, const u32
   // Tiles that reach past T-W: same pipeline with the causal mask.
   for (; kt < n_tiles; ++kt) {
     const u32x4* buf = ks[kt & 1];
-    if (wave_active) {
-      rs_step<D, true>(cx, buf, 0, accA, accB, kt * kRsTile - 32, c, j, h);
-      rs_step<D, true>(cx, buf, 1, accB, accA, kt * kRsTile, c, j, h);
-    }
+    if (wave_active) rs_tile<D, true>(cx, buf, accA, accB, kt * kRsTile, c, j, h);
     // Unconditional (past the end: a clamped reload into the idle buffer) so
     // the loop body stays one basic block for the MFMA/VALU interleave.
     stash((kt + 1) & 1, pre);
@@ -317,27 +330,23 @@ __device__ __forceinline__ void col_update(const f32x16& a0, const f32x16& a1,
 }
 
 template <int D, bool MASK>
-__device__ __forceinline__ void cs_step(CsCtx<D>& cx, const u32x4* __restrict__ buf, int bi,
-                                        f32x16& a0, f32x16& a1, const f32x16& p0,
-                                        const f32x16& p1, const float* __restrict__ pb,
-                                        int pwbase, float c, int T, int W, int j, int h) {
-  constexpr int kStride = D / 8 + 1;
+__device__ __forceinline__ void cs_step(CsCtx<D>& cx, const u32x4 (&fa)[D / 16], f32x16& a0,
+                                        f32x16& a1, const f32x16& p0, const f32x16& p1,
+                                        const float* __restrict__ pb, int pwbase, float c, int T,
+                                        int W, int h) {
   a0 = f32x16{};
   a1 = f32x16{};
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    const u32x4 a = buf[(bi * 32 + j) * kStride + h * (D / 16) + s];
-    a0 = mfma32(a, cx.kop[0][s], a0);
-    a1 = mfma32(a, cx.kop[1][s], a1);
+    a0 = mfma32(fa[s], cx.kop[0][s], a0);
+    a1 = mfma32(fa[s], cx.kop[1][s], a1);
   }
   col_update<MASK>(p0, p1, pb, c, T, W, pwbase, cx.key0, h, cx.cs0, cx.cs1);
-  // Interleave: the normaliser reads and LDS reads one k-step ahead, then two
-  // MFMAs and ~12 VALU per step.
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+  // The four normaliser reads first, then two MFMAs and ~12 VALU per k-step.
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedValu, 12, 0);
   }
 }
@@ -386,10 +395,13 @@ __device__ void cs_run(CsCtx<D>& cx, u32x4 (*qs)[kCsBatch * 32 * (D / 8 + 1)],
   for (; bt < full_batches; ++bt) {
     const u32x4* buf = qs[bt & 1];
     const int blk = bt * kCsBatch;
-    cs_step<D, MASK>(cx, buf, 0, a0A, a1A, a0B, a1B, bsh + (blk > 0 ? blk - 1 : 0) * 32,
-                     ((blk - 1 + n_blocks) % n_rb) * 32, c, T, W, j, h);
-    cs_step<D, MASK>(cx, buf, 1, a0B, a1B, a0A, a1A, bsh + blk * 32, (blk % n_rb) * 32, c, T, W,
-                     j, h);
+    u32x4 f0[D / 16], f1[D / 16];
+    load_frags<D>(buf, 0, j, h, f0);
+    load_frags<D>(buf, 1, j, h, f1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * (D / 16), 0);
+    cs_step<D, MASK>(cx, f0, a0A, a1A, a0B, a1B, bsh + (blk > 0 ? blk - 1 : 0) * 32,
+                     ((blk - 1 + n_blocks) % n_rb) * 32, c, T, W, h);
+    cs_step<D, MASK>(cx, f1, a0B, a1B, a0A, a1A, bsh + blk * 32, (blk % n_rb) * 32, c, T, W, h);
     stash((bt + 1) & 1, pre);  // unconditional: see k_rowstats
     fetch(bt + 2, pre);
     __syncthreads();
@@ -398,8 +410,10 @@ __device__ void cs_run(CsCtx<D>& cx, u32x4 (*qs)[kCsBatch * 32 * (D / 8 + 1)],
   if (bt < n_batches) {                    // odd block count: one more block
     const u32x4* buf = qs[bt & 1];
     const int blk = bt * kCsBatch;
-    cs_step<D, MASK>(cx, buf, 0, a0A, a1A, a0B, a1B, bsh + (blk > 0 ? blk - 1 : 0) * 32,
-                     ((blk - 1 + n_blocks) % n_rb) * 32, c, T, W, j, h);
+    u32x4 f0[D / 16];
+    load_frags<D>(buf, 0, j, h, f0);
+    cs_step<D, MASK>(cx, f0, a0A, a1A, a0B, a1B, bsh + (blk > 0 ? blk - 1 : 0) * 32,
+                     ((blk - 1 + n_blocks) % n_rb) * 32, c, T, W, h);
     col_update<MASK>(a0A, a1A, bsh + blk * 32, c, T, W, (blk % n_rb) * 32, cx.key0, h, cx.cs0,
                      cx.cs1);
   } else if (last >= 0) {

@@ -18,7 +18,7 @@
 namespace kvc {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kWaveSeg = 256;  // segments up to this length: one wave each
 constexpr int kPerLane = kWaveSeg / 64;
