@@ -83,6 +83,20 @@ def algorithmic(wl) -> dict:
                 b_gather=b_gather, b_total=b_score + b_mass + b_select + b_gather)
 
 
+def recorded_traffic(workload: str):
+    """HBM bytes per score-stage launch from the committed counter runs
+    (profiles/traffic_<workload>.json), or None when the score kernels have
+    changed since the counters were taken (source hash mismatch)."""
+    import hashlib
+    f = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(f):
+        return None
+    rec = json.load(open(f))
+    src = os.path.join(ROOT, "eviction_window_qk_amd", "csrc", "kvc_score.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return rec["score_stage_traffic_bytes"] if rec.get("score_source_sha256_16") == h else None
+
+
 def _oracle_head(args):
     name, n = args
     from eviction_window_qk_amd import synth
@@ -100,13 +114,14 @@ def _oracle_head(args):
 
 
 def cpu_baseline(name: str, n_heads: int, cores: int) -> dict:
-    """The oracle, as it stands, on the first n_heads heads of the workload."""
+    """The oracle, as it stands, on n_heads head-events of the workload (cycling
+    through its heads: 2 * n_heads of the workload = two whole events)."""
     import multiprocessing as mp
     from eviction_window_qk_amd import synth
     wl = synth.WORKLOADS[name]
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"
-    heads = list(range(min(n_heads, wl.n_heads)))
+    heads = [i % wl.n_heads for i in range(n_heads)]
     ctx = mp.get_context("spawn")
     with ctx.Pool(cores) as pool:
         pool.map(_oracle_head, [(name, 0)] * cores)           # warm the workers
@@ -115,9 +130,10 @@ def cpu_baseline(name: str, n_heads: int, cores: int) -> dict:
         wall = time.perf_counter() - t0
     tokens = len(heads) * wl.T
     return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(heads)} of {wl.n_heads} head-events of {name} (T={wl.T}), full "
-                      f"oracle event per head (fp64 score + exact steps 2-5), {cores} worker "
-                      f"processes x 1 thread; {sum(busy):.1f} s of CPU work in {wall:.1f} s wall"}
+            "sample": f"{len(heads)} head-events ({len(heads) / wl.n_heads:.2f} events of {name}, "
+                      f"{wl.n_heads} head-events each, T={wl.T}): full oracle event per head (fp64 "
+                      f"score + exact steps 2-5), {cores} worker processes x 1 thread; "
+                      f"{sum(busy):.1f} s of CPU work in {wall:.1f} s wall"}
 
 
 def main():
@@ -127,7 +143,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen7b_t768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=512)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="head-events in the CPU oracle sample (default: two whole events)")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (the event is independent per head "
@@ -140,6 +159,16 @@ def main():
 
     if not torch.cuda.is_available():
         sys.exit("bench.py: no GPU visible")
+    if args.copy_probe:
+        # A plain device-to-device copy of known size: what FETCH_SIZE/WRITE_SIZE
+        # read for it calibrates the traffic counters.
+        src = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}))
+        return
     wl = synth.WORKLOADS[args.workload]
     cores = min(len(os.sched_getaffinity(0)), 16)
     t_gen = time.perf_counter()
@@ -243,7 +272,8 @@ def main():
                    "head_dim": wl.head_dim, "T": wl.T, "window": wl.window,
                    "budget": wl.budget, "ema": ema, "seed": wl.seed},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": recorded_traffic(wl.name),
                      "kernel": "score stage (k_rowstats + k_colsum + k_fill)",
                      "algorithmic_flops_per_launch": alg["flops"]},
         "events_per_s": 1000.0 / ms,
@@ -255,7 +285,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_heads, cores)
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_heads or 2 * wl.n_heads, cores)
     print(json.dumps(line), flush=True)
 
 
