@@ -147,3 +147,33 @@ def check_kept_valid(kept: np.ndarray, pd: dict, T: int):
         assert np.all(np.diff(valid) > 0) and valid[0] >= 0 and valid[-1] < T
         must = set(range(s)) | set(range(T - r, T))
         assert must <= set(valid.tolist())
+
+
+def _gen_chunk(args):
+    name, heads, seed, T = args
+    return synth.gen_heads(synth.WORKLOADS[name], heads, T=T, seed=seed)
+
+
+def gen_all(name: str, seed=None, T=None, workers: int = 16, chunk: int = 16):
+    """Every head-event of a workload (bf16 bits), generated in parallel; prints
+    progress so a long generation is visibly alive."""
+    import multiprocessing as mp
+    import os
+    import time
+    wl = synth.WORKLOADS[name]
+    T = wl.T if T is None else T
+    heads = list(range(wl.n_heads))
+    chunks = [heads[i:i + chunk] for i in range(0, len(heads), chunk)]
+    q = np.empty((wl.n_heads, wl.group, wl.window, wl.head_dim), np.uint16)
+    k = np.empty((wl.n_heads, T, wl.head_dim), np.uint16)
+    v = np.empty((wl.n_heads, T, wl.head_dim), np.uint16)
+    workers = max(1, min(workers, len(os.sched_getaffinity(0))))
+    t0 = time.time()
+    with mp.get_context("spawn").Pool(workers) as pool:
+        for i, (c, (qq, kk, vv)) in enumerate(zip(chunks, pool.imap(
+                _gen_chunk, [(name, c, seed, T) for c in chunks]))):
+            q[c[0]:c[-1] + 1], k[c[0]:c[-1] + 1], v[c[0]:c[-1] + 1] = qq, kk, vv
+            if (i + 1) % max(1, len(chunks) // 8) == 0:
+                print(f"[gen] {name}: {c[-1] + 1}/{wl.n_heads} heads, {time.time() - t0:.1f} s",
+                      flush=True)
+    return q, k, v
