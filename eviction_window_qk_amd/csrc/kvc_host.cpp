@@ -114,6 +114,7 @@ static int derive(const kvc_params* p, Derived* d) {
   d->s_cap = int(cap);
   const double scale = p->scale != 0.0f ? double(p->scale) : 1.0 / sqrt(double(p->head_dim));
   d->c_log2 = float(scale * 1.4426950408889634);  // scale * log2(e)
+  if (!(d->c_log2 >= 0x1p-60f)) return KVC_EINVAL;  // the score kernels need c >= 2^-60
   d->eps_q = uint64_t(ceil(p->eps * 1099511627776.0));  // ceil(eps * 2^40)
   d->delta = p->delta;
   d->lam = p->lambda;

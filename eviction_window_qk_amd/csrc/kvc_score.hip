@@ -29,12 +29,14 @@
 //               the fully observed ones.
 //
 // Per score element the VALU work is one FMA, one exp2 and one add (plus half
-// a max in pass 1).  Both passes are software-pipelined: the MFMAs of one
-// 32-wide block are issued interleaved with the softmax arithmetic of the
-// previous block, so the matrix cores and the vector ALUs of a SIMD work at
-// the same time even within one wave.  The causal mask costs nothing on
-// blocks every row sees fully; only blocks reaching past T-W take the masked
-// loop.  No atomics: every sum has a fixed order, so u is bitwise
+// a max in pass 1); the exp2 is the costliest of them, and on gfx950 the
+// vector ALU port, not the matrix core, bounds both passes.  Each wave issues
+// the MFMAs of one 32x32 block and then its softmax arithmetic; three waves
+// per SIMD (at most 168 VGPRs) let one wave's MFMAs run under another wave's
+// VALU work.  Every (32-row, 32-key) block is classified against the causal
+// limits of its rows: blocks no row sees are skipped (MFMAs included), blocks
+// every row sees fully take the unmasked update, only the diagonal ones pay
+// for the mask.  No atomics: every sum has a fixed order, so u is bitwise
 // reproducible.  Blocks are renumbered so that the workgroups of one head
 // share an XCD and its L2.
 #include "kvc_internal.h"
@@ -48,11 +50,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;
-
-// sched_group_barrier masks
-constexpr int kSchedValu = 0x002;
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -95,40 +92,48 @@ constexpr int kRsTile = 64;                             // keys per LDS tile (tw
 constexpr int kRsThreads = 64 * kRsWaves;
 
 // Online max/sum update of one row (this lane's) with 16 new raw dot products.
+// m starts at the finite floor m_floor() instead of -inf, so no guards are
+// needed: the first visible key replaces it and the old l (0) is scaled by 0;
+// masked entries are -inf and add exp2(-inf) = 0.  The rescale factor is formed
+// from m - mx, which is exactly 0 while the maximum stands.
 template <bool MASK>
 __device__ __forceinline__ void row_update(f32x16 acc, float c, int t0, int h, int lim, float& m,
                                            float& l) {
   if (MASK) {
+    const int d = lim - t0 - 4 * h;
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (t0 + acc_row(r, h) > lim) acc[r] = -INFINITY;
+      if (8 * (r >> 2) + (r & 3) > d) acc[r] = -INFINITY;
   }
-  float mx = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+  float mx = fmaxf(fmaxf(m, acc[0]), acc[1]);
 #pragma unroll
-  for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
-  mx = fmaxf(mx, acc[15]);
-  const float mn = fmaxf(m, mx);
-  // mn is -inf only while every key seen so far is masked (then l stays 0).
-  const float nb = mn == -INFINITY ? 0.0f : -mn * c;
-  float s0 = 0.0f, s1 = 0.0f;
+  for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+  const float nb = -mx * c;
+  float s0 = fast_exp2(__builtin_fmaf(acc[0], c, nb));
+  float s1 = fast_exp2(__builtin_fmaf(acc[1], c, nb));
 #pragma unroll
-  for (int r = 0; r < 16; r += 2) {
+  for (int r = 2; r < 16; r += 2) {
     s0 += fast_exp2(__builtin_fmaf(acc[r], c, nb));
     s1 += fast_exp2(__builtin_fmaf(acc[r + 1], c, nb));
   }
-  const float scale = m == -INFINITY ? 0.0f : fast_exp2(__builtin_fmaf(m, c, nb));
+  const float scale = fast_exp2((m - mx) * c);
   l = __builtin_fmaf(l, scale, s0 + s1);
-  m = mn;
+  m = mx;
 }
+
+// Starting value of the running maximum: below every finite dot product the
+// inputs can produce in practice, with m_floor * c = -2^64 finite.  The host
+// rejects c < 2^-60, so the quotient is finite.
+__device__ __forceinline__ float m_floor(float c) { return -0x1p64f / c; }
 
 template <int D>
 struct RsCtx {
   u32x4 qop[kRsRowBlocks][D / 16];
   float m[kRsRowBlocks], l[kRsRowBlocks];
   int lim[kRsRowBlocks];
+  int lo[kRsRowBlocks], hi[kRsRowBlocks];  // wave-uniform min/max of lim per row block
 };
 
-// A-operand fragments (one 32-key block) of k-steps 0..D/16-1 from LDS.
 template <int D>
 __device__ __forceinline__ void load_frags(const u32x4* __restrict__ buf, int blk, int j, int h,
                                            u32x4 (&f)[D / 16]) {
@@ -137,47 +142,56 @@ __device__ __forceinline__ void load_frags(const u32x4* __restrict__ buf, int bl
   for (int s = 0; s < D / 16; ++s) f[s] = buf[(blk * 32 + j) * kStride + h * (D / 16) + s];
 }
 
-// MFMAs of one 32-key block (fragments already in registers) into acc,
-// interleaved with the softmax of the previous block (pacc, keys from pt0).
-template <int D, bool MASK>
-__device__ __forceinline__ void rs_step(RsCtx<D>& cx, const u32x4 (&fa)[D / 16],
-                                        f32x16 (&acc)[kRsRowBlocks],
-                                        const f32x16 (&pacc)[kRsRowBlocks], int pt0, float c,
-                                        int h) {
+__device__ __forceinline__ int wave_min(int x) {
 #pragma unroll
-  for (int rb = 0; rb < kRsRowBlocks; ++rb) acc[rb] = f32x16{};
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-    for (int rb = 0; rb < kRsRowBlocks; ++rb) acc[rb] = mfma32(fa[s], cx.qop[rb][s], acc[rb]);
-  }
-#pragma unroll
-  for (int rb = 0; rb < kRsRowBlocks; ++rb)
-    row_update<MASK>(pacc[rb], c, pt0, h, cx.lim[rb], cx.m[rb], cx.l[rb]);
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kRsRowBlocks, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, 15, 0);
-  }
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return __builtin_amdgcn_readfirstlane(x);
 }
-
-// One 64-key LDS tile: both blocks' fragments are read up front, then
-// MFMA(block 0) || softmax(previous block), MFMA(block 1) || softmax(block 0).
-template <int D, bool MASK>
-__device__ __forceinline__ void rs_tile(RsCtx<D>& cx, const u32x4* __restrict__ buf,
-                                        f32x16 (&accA)[kRsRowBlocks],
-                                        f32x16 (&accB)[kRsRowBlocks], int t0, float c, int j,
-                                        int h) {
-  u32x4 f0[D / 16], f1[D / 16];
-  load_frags<D>(buf, 0, j, h, f0);
-  load_frags<D>(buf, 1, j, h, f1);
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * (D / 16), 0);
-  rs_step<D, MASK>(cx, f0, accA, accB, t0 - 32, c, h);
-  rs_step<D, MASK>(cx, f1, accB, accA, t0, c, h);
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return __builtin_amdgcn_readfirstlane(x);
 }
 
 template <int D>
-__global__ __launch_bounds__(kRsThreads, 2) void k_rowstats(Derived P, const u32x4* __restrict__ q,
+__device__ __forceinline__ void rs_update(RsCtx<D>& cx, int rb, const f32x16& acc, int t0,
+                                          float c, int h) {
+  if (t0 + 31 <= cx.lo[rb])
+    row_update<false>(acc, c, t0, h, cx.lim[rb], cx.m[rb], cx.l[rb]);
+  else
+    row_update<true>(acc, c, t0, h, cx.lim[rb], cx.m[rb], cx.l[rb]);
+}
+
+// One 32-key block: fragments from LDS, MFMAs for the row blocks that see
+// any of its keys, then the online update.  Row blocks that see none of the
+// keys are skipped (their update would leave m and l unchanged).
+template <int D>
+__device__ __forceinline__ void rs_block(RsCtx<D>& cx, const u32x4* __restrict__ buf, int blk,
+                                         int t0, float c, int j, int h) {
+  const bool a0 = t0 <= cx.hi[0], a1 = t0 <= cx.hi[1];
+  if (!a0 && !a1) return;
+  u32x4 f[D / 16];
+  load_frags<D>(buf, blk, j, h, f);
+  if (a0 && a1) {
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      acc0 = mfma32(f[s], cx.qop[0][s], acc0);
+      acc1 = mfma32(f[s], cx.qop[1][s], acc1);
+    }
+    rs_update<D>(cx, 0, acc0, t0, c, h);
+    rs_update<D>(cx, 1, acc1, t0, c, h);
+  } else {
+    const int rb = a0 ? 0 : 1;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) acc = mfma32(f[s], a0 ? cx.qop[0][s] : cx.qop[1][s], acc);
+    rs_update<D>(cx, rb, acc, t0, c, h);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kRsThreads, 3) void k_rowstats(Derived P, const u32x4* __restrict__ q,
                                                             const u32x4* __restrict__ k,
                                                             float* __restrict__ rowb) {
   constexpr int kPerRow = D / 8;        // u32x4 per row
@@ -201,15 +215,15 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_rowstats(Derived P, const u32
     const int r = row0 + rb * 32 + j;
     const int rc = r < R ? r : R - 1;  // padding rows duplicate a real row, never written
     cx.lim[rb] = T - W + rc % W;
+    cx.lo[rb] = wave_min(cx.lim[rb]);
+    cx.hi[rb] = wave_max(cx.lim[rb]);
     load_rows_op<D>(q + size_t(n) * R * kPerRow, rc, h, cx.qop[rb]);
-    cx.m[rb] = -INFINITY;
+    cx.m[rb] = m_floor(c);
     cx.l[rb] = 0.0f;
   }
 
   const u32x4* kn = k + size_t(n) * P.TS * kPerRow;
   const int n_tiles = (T + kRsTile - 1) / kRsTile;
-  // Tiles whose every key is seen by every row (t <= T-W) need no mask.
-  const int n_full = (T - W + 1) / kRsTile;
   auto fetch = [&](int kt, u32x4 (&pre)[kLoads]) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -233,50 +247,29 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_rowstats(Derived P, const u32
   if (n_tiles > 1) fetch(1, pre);
   __syncthreads();
 
-  // accB starts as a pending block of -inf: its update leaves (m, l) unchanged.
-  f32x16 accA[kRsRowBlocks], accB[kRsRowBlocks];
-#pragma unroll
-  for (int rb = 0; rb < kRsRowBlocks; ++rb) {
-    accA[rb] = f32x16{};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) accB[rb][r] = -INFINITY;
-  }
-  int kt = 0;
-  // Unmasked tiles: two 32-key blocks each, pipelined across blocks and tiles.
-  for (; kt < n_full; ++kt) {
+  for (int kt = 0; kt < n_tiles; ++kt) {
     const u32x4* buf = ks[kt & 1];
-    if (wave_active) rs_tile<D, false>(cx, buf, accA, accB, kt * kRsTile, c, j, h);
-    // Unconditional (past the end: a clamped reload into the idle buffer) so
-    // the loop body stays one basic block for the MFMA/VALU interleave.
-    stash((kt + 1) & 1, pre);
-    fetch(kt + 2, pre);
-    __syncthreads();
-  }
-  // Tiles that reach past T-W: same pipeline with the causal mask.
-  for (; kt < n_tiles; ++kt) {
-    const u32x4* buf = ks[kt & 1];
-    if (wave_active) rs_tile<D, true>(cx, buf, accA, accB, kt * kRsTile, c, j, h);
-    // Unconditional (past the end: a clamped reload into the idle buffer) so
-    // the loop body stays one basic block for the MFMA/VALU interleave.
-    stash((kt + 1) & 1, pre);
-    fetch(kt + 2, pre);
+    if (wave_active) {
+      rs_block<D>(cx, buf, 0, kt * kRsTile, c, j, h);
+      rs_block<D>(cx, buf, 1, kt * kRsTile + 32, c, j, h);
+    }
+    if (kt + 1 < n_tiles) {
+      stash((kt + 1) & 1, pre);
+      if (kt + 2 < n_tiles) fetch(kt + 2, pre);
+    }
     __syncthreads();
   }
   if (!wave_active) return;
-  // Last block still pending in accB (keys from (n_tiles-1)*64 + 32).
-#pragma unroll
-  for (int rb = 0; rb < kRsRowBlocks; ++rb)
-    row_update<true>(accB[rb], c, (n_tiles - 1) * kRsTile + 32, h, cx.lim[rb], cx.m[rb], cx.l[rb]);
 
-  // Merge the two lane halves (same row, different keys) and write b.
+  // Merge the two lane halves (same row, different keys) and write b.  Key 0
+  // is visible to every row, so at least one half holds a real maximum; a
+  // half that saw no key has l = 0 and m = m_floor.
 #pragma unroll
   for (int rb = 0; rb < kRsRowBlocks; ++rb) {
     const float mo = __shfl_xor(cx.m[rb], 32);
     const float lo = __shfl_xor(cx.l[rb], 32);
     const float mm = fmaxf(cx.m[rb], mo);
-    float ll = 0.0f;
-    if (cx.m[rb] != -INFINITY) ll += cx.l[rb] * fast_exp2((cx.m[rb] - mm) * c);
-    if (mo != -INFINITY) ll += lo * fast_exp2((mo - mm) * c);
+    const float ll = cx.l[rb] * fast_exp2((cx.m[rb] - mm) * c) + lo * fast_exp2((mo - mm) * c);
     const int r = row0 + rb * 32 + j;
     if (h == 0 && r < R) rowb[size_t(n) * R + r] = mm * c + __log2f(ll);
   }
@@ -297,64 +290,73 @@ struct CsCtx {
   int key0;  // this lane's first key (second is key0 + 32)
 };
 
-// Column sums of one 32-row block's probabilities (accumulators a0/a1, row
-// normalisers bblk[0..32) in LDS).
+// Column-sum contribution of one 32-row block to one 32-key block (this
+// lane's key), normalisers b[] of the block's rows already in registers.
 template <bool MASK>
-__device__ __forceinline__ void col_update(const f32x16& a0, const f32x16& a1,
-                                           const float* __restrict__ bblk, float c, int T, int W,
-                                           int wbase, int key0, int h, float& cs0, float& cs1) {
-  float b[16];
-#pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) {
-    const f32x4 bb = *reinterpret_cast<const f32x4*>(&bblk[8 * i4 + 4 * h]);
-    b[4 * i4 + 0] = bb[0];
-    b[4 * i4 + 1] = bb[1];
-    b[4 * i4 + 2] = bb[2];
-    b[4 * i4 + 3] = bb[3];
-  }
-  float s0 = 0.0f, s1 = 0.0f;
+__device__ __forceinline__ void col_update1(const f32x16& a, const float (&b)[16], float c, int lim0,
+                                            int key, int h, float& cs) {
+  float s0, s1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    float x0 = __builtin_fmaf(a0[r], c, -b[r]);
-    float x1 = __builtin_fmaf(a1[r], c, -b[r]);
-    if (MASK) {
-      const int lim = T - W + wbase + acc_row(r, h);
-      x0 = key0 > lim ? -INFINITY : x0;
-      x1 = key0 + 32 > lim ? -INFINITY : x1;
+    float x = __builtin_fmaf(a[r], c, -b[r]);
+    if (MASK) x = key > lim0 + acc_row(r, h) ? -INFINITY : x;
+    const float p = fast_exp2(x);
+    if (r == 0) s0 = p;
+    else if (r == 1) s1 = p;
+    else if (r & 1) s1 += p;
+    else s0 += p;
+  }
+  cs += s0 + s1;
+}
+
+template <int D>
+__device__ __forceinline__ void cs_block(CsCtx<D>& cx, const u32x4* __restrict__ buf, int bi,
+                                         const float* __restrict__ bblk, int lim_lo, float c,
+                                         int kbase, int j, int h) {
+  // lim of the block's rows runs over [lim_lo, lim_lo + 31]; keys of block kb
+  // are kbase + 32 kb + [0, 32).
+  const bool dead0 = kbase > lim_lo + 31, dead1 = kbase + 32 > lim_lo + 31;
+  if (dead0) return;  // dead0 implies dead1
+  const bool vis0 = kbase + 31 <= lim_lo, vis1 = kbase + 63 <= lim_lo;
+  u32x4 f[D / 16];
+  load_frags<D>(buf, bi, j, h, f);
+  float b[16];
+  auto load_b = [&]() {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(&bblk[8 * i4 + 4 * h]);
+      b[4 * i4 + 0] = bb[0];
+      b[4 * i4 + 1] = bb[1];
+      b[4 * i4 + 2] = bb[2];
+      b[4 * i4 + 3] = bb[3];
     }
-    s0 += fast_exp2(x0);
-    s1 += fast_exp2(x1);
-  }
-  cs0 += s0;
-  cs1 += s1;
-}
-
-template <int D, bool MASK>
-__device__ __forceinline__ void cs_step(CsCtx<D>& cx, const u32x4 (&fa)[D / 16], f32x16& a0,
-                                        f32x16& a1, const f32x16& p0, const f32x16& p1,
-                                        const float* __restrict__ pb, int pwbase, float c, int T,
-                                        int W, int h) {
-  a0 = f32x16{};
-  a1 = f32x16{};
+  };
+  if (!dead1) {
+    f32x16 a0 = f32x16{}, a1 = f32x16{};
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    a0 = mfma32(fa[s], cx.kop[0][s], a0);
-    a1 = mfma32(fa[s], cx.kop[1][s], a1);
-  }
-  col_update<MASK>(p0, p1, pb, c, T, W, pwbase, cx.key0, h, cx.cs0, cx.cs1);
-  // The four normaliser reads first, then two MFMAs and ~12 VALU per k-step.
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+    for (int s = 0; s < D / 16; ++s) {
+      a0 = mfma32(f[s], cx.kop[0][s], a0);
+      a1 = mfma32(f[s], cx.kop[1][s], a1);
+    }
+    load_b();
+    if (vis0) col_update1<false>(a0, b, c, lim_lo, cx.key0, h, cx.cs0);
+    else col_update1<true>(a0, b, c, lim_lo, cx.key0, h, cx.cs0);
+    if (vis1) col_update1<false>(a1, b, c, lim_lo, cx.key0 + 32, h, cx.cs1);
+    else col_update1<true>(a1, b, c, lim_lo, cx.key0 + 32, h, cx.cs1);
+  } else {
+    f32x16 a0 = f32x16{};
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, 12, 0);
+    for (int s = 0; s < D / 16; ++s) a0 = mfma32(f[s], cx.kop[0][s], a0);
+    load_b();
+    if (vis0) col_update1<false>(a0, b, c, lim_lo, cx.key0, h, cx.cs0);
+    else col_update1<true>(a0, b, c, lim_lo, cx.key0, h, cx.cs0);
   }
 }
 
-template <int D, bool MASK>
+template <int D>
 __device__ void cs_run(CsCtx<D>& cx, u32x4 (*qs)[kCsBatch * 32 * (D / 8 + 1)],
                        const float* __restrict__ bsh, const u32x4* __restrict__ qn, int n_blocks,
-                       int n_rb, float c, int T, int W, int j, int h) {
+                       int n_rb, float c, int T, int W, int kbase, int j, int h) {
   constexpr int kPerRow = D / 8;
   constexpr int kStride = kPerRow + 1;
   constexpr int kLoads = kCsBatch * 32 * kPerRow / kCsThreads;
@@ -384,46 +386,24 @@ __device__ void cs_run(CsCtx<D>& cx, u32x4 (*qs)[kCsBatch * 32 * (D / 8 + 1)],
   stash(0, pre);
   if (n_batches > 1) fetch(1, pre);
   __syncthreads();
-
-  // (a0B, a1B) start as a pending block of -inf: its column sums add +0.0.
-  f32x16 a0A, a1A, a0B, a1B;
-  a0A = a1A = f32x16{};
+  for (int bt = 0; bt < n_batches; ++bt) {
+    const u32x4* buf = qs[bt & 1];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) a0B[r] = a1B[r] = -INFINITY;
-  const int full_batches = n_blocks / kCsBatch;
-  int bt = 0;
-  for (; bt < full_batches; ++bt) {
-    const u32x4* buf = qs[bt & 1];
-    const int blk = bt * kCsBatch;
-    u32x4 f0[D / 16], f1[D / 16];
-    load_frags<D>(buf, 0, j, h, f0);
-    load_frags<D>(buf, 1, j, h, f1);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * (D / 16), 0);
-    cs_step<D, MASK>(cx, f0, a0A, a1A, a0B, a1B, bsh + (blk > 0 ? blk - 1 : 0) * 32,
-                     ((blk - 1 + n_blocks) % n_rb) * 32, c, T, W, h);
-    cs_step<D, MASK>(cx, f1, a0B, a1B, a0A, a1A, bsh + blk * 32, (blk % n_rb) * 32, c, T, W, h);
-    stash((bt + 1) & 1, pre);  // unconditional: see k_rowstats
-    fetch(bt + 2, pre);
+    for (int bi = 0; bi < kCsBatch; ++bi) {
+      const int blk = bt * kCsBatch + bi;
+      if (blk < n_blocks)
+        cs_block<D>(cx, buf, bi, bsh + blk * 32, T - W + (blk % n_rb) * 32, c, kbase, j, h);
+    }
+    if (bt + 1 < n_batches) {
+      stash((bt + 1) & 1, pre);
+      if (bt + 2 < n_batches) fetch(bt + 2, pre);
+    }
     __syncthreads();
-  }
-  int last = full_batches * kCsBatch - 1;  // block pending in (a0B, a1B)
-  if (bt < n_batches) {                    // odd block count: one more block
-    const u32x4* buf = qs[bt & 1];
-    const int blk = bt * kCsBatch;
-    u32x4 f0[D / 16];
-    load_frags<D>(buf, 0, j, h, f0);
-    cs_step<D, MASK>(cx, f0, a0A, a1A, a0B, a1B, bsh + (blk > 0 ? blk - 1 : 0) * 32,
-                     ((blk - 1 + n_blocks) % n_rb) * 32, c, T, W, h);
-    col_update<MASK>(a0A, a1A, bsh + blk * 32, c, T, W, (blk % n_rb) * 32, cx.key0, h, cx.cs0,
-                     cx.cs1);
-  } else if (last >= 0) {
-    col_update<MASK>(a0B, a1B, bsh + last * 32, c, T, W, (last % n_rb) * 32, cx.key0, h, cx.cs0,
-                     cx.cs1);
   }
 }
 
 template <int D, bool SUM>
-__global__ __launch_bounds__(kCsThreads, 2) void k_colsum(Derived P, const u32x4* __restrict__ q,
+__global__ __launch_bounds__(kCsThreads, SUM ? 3 : 2) void k_colsum(Derived P, const u32x4* __restrict__ q,
                                                           const u32x4* __restrict__ k,
                                                           const float* __restrict__ rowb,
                                                           float* __restrict__ u) {
@@ -441,8 +421,6 @@ __global__ __launch_bounds__(kCsThreads, 2) void k_colsum(Derived P, const u32x4
   const float c = P.c_log2;
   const int key_base = chunk * kCsKeys + wave * kScoreKeysPerWave;
 
-  // Row blocks enumerate (g, rb) so that no block straddles two query heads:
-  // block i covers window slots [rb*32, min(W, rb*32+32)) of head g.
   const int n_rb = (W + 31) / 32;
   const int n_blocks = G * n_rb;
   for (int i = threadIdx.x; i < n_blocks * 32; i += kCsThreads) {
@@ -463,20 +441,16 @@ __global__ __launch_bounds__(kCsThreads, 2) void k_colsum(Derived P, const u32x4
 
   if (SUM) {
     cx.cs0 = cx.cs1 = 0.0f;
-    // Masking is needed only when some key of this wave lies past T-W (or T).
-    const bool mask = key_base + kScoreKeysPerWave - 1 > T - W;
-    if (mask) cs_run<D, true>(cx, qs, bsh, qn, n_blocks, n_rb, c, T, W, j, h);
-    else cs_run<D, false>(cx, qs, bsh, qn, n_blocks, n_rb, c, T, W, j, h);
+    cs_run<D>(cx, qs, bsh, qn, n_blocks, n_rb, c, T, W, key_base, j, h);
     cx.cs0 += __shfl_xor(cx.cs0, 32);
     cx.cs1 += __shfl_xor(cx.cs1, 32);
   } else {
-    // MAX over the query heads: one head's blocks at a time.
     float tot0 = -INFINITY, tot1 = -INFINITY;
     for (int g = 0; g < G; ++g) {
       cx.cs0 = cx.cs1 = 0.0f;
       __syncthreads();  // previous head's LDS use done
-      cs_run<D, true>(cx, qs, bsh + g * n_rb * 32, qn + size_t(g) * W * kPerRow, n_rb, n_rb, c,
-                      T, W, j, h);
+      cs_run<D>(cx, qs, bsh + g * n_rb * 32, qn + size_t(g) * W * kPerRow, n_rb, n_rb, c, T, W,
+                key_base, j, h);
       tot0 = fmaxf(tot0, cx.cs0 + __shfl_xor(cx.cs0, 32));
       tot1 = fmaxf(tot1, cx.cs1 + __shfl_xor(cx.cs1, 32));
     }

@@ -96,7 +96,8 @@ typedef struct kvc_params {
   int32_t head_agg;    /* KVC_AGG_SUM or KVC_AGG_MAX over the G query heads  */
   int32_t ema;         /* 1 = EMA credit on, 0 = off                         */
   int32_t n_prev;      /* credit entries carried per head (0..T; 0 if !ema)  */
-  float scale;         /* softmax scale; 0 => 1/sqrt(head_dim)               */
+  float scale;         /* softmax scale; 0 => 1/sqrt(head_dim); otherwise
+                          finite with scale*log2(e) >= 2^-60                 */
   double delta;        /* target segment mass Delta in (0, inf); >= 1 => no
                           mass cuts; at most 1024 thresholds                 */
   double lambda;       /* EMA decay, [0,1], e.g. 0.9                          */

@@ -69,7 +69,8 @@ def _p(**kw):
     (dict(pool_kernel=65), -1), (dict(pool_mode=2), -1), (dict(head_agg=3), -1),
     (dict(lam=1.5), -1), (dict(beta=-0.1), -1), (dict(eps=0.0), -1), (dict(eps=2.0), -1),
     (dict(n_prev=5), -1),                    # credit without EMA
-    (dict(ema=True, n_prev=769), -1), (dict(scale=-1.0), -1),
+    (dict(ema=True, n_prev=769), -1), (dict(scale=-1.0), -1), (dict(scale=1e-20), -1),
+    (dict(scale=float("inf")), -1),
     (dict(window=128, group=64), -1),        # W*G > 4096
     (dict(T=2048, window=512, group=8), -1), # W*G = 4096 but 7*W*W*G >= 2^22
     (dict(n_heads=-1), -1),
