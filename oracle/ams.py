@@ -53,6 +53,8 @@ POOL_AVG = 0
 POOL_MAX = 1
 AGG_SUM = 0
 AGG_MAX = 1
+QUOTA_MASS = 0      # remainder split by segment mass (the method)
+QUOTA_UNIFORM = 1   # ablation: the same weight for every segment
 
 USAGE_SHIFT = 40      # usage fixed point: a_t = trunc(ubar_t * 2^40)
 CREDIT_SHIFT = 44     # credit / mixed-mass fixed point (Q44)
@@ -90,6 +92,8 @@ class Params:
     eps: float = 1e-6
     n_prev: int = 0
     scale: float = 0.0            # 0 => 1/sqrt(head_dim)
+    seg_fixed: int = 0            # ablation: > 0 => fixed-length raw segments
+    quota_mode: int = QUOTA_MASS  # ablation: QUOTA_UNIFORM => no mass weighting
 
     def with_(self, **kw) -> "Params":
         return replace(self, **kw)
@@ -312,6 +316,16 @@ def raw_cuts(P: np.ndarray, delta: float):
     return sorted(ends)
 
 
+def fixed_cuts(T: int, length: int):
+    """Ablation "fixed-length segments" [AMS notes, ablations, Table 7]: the
+    mass-driven cuts are replaced by cuts every `length` positions.  Reading:
+    raw segments [0,L), [L,2L), ..., the last one ending at T-1 (possibly
+    shorter); merge and split then run exactly as for mass cuts."""
+    ends = list(range(length - 1, T - 1, length))
+    ends.append(T - 1)
+    return ends
+
+
 def segments_from_ends(ends):
     segs = []
     start = 0
@@ -367,15 +381,22 @@ def split_long(segs, seg_max: int):
 
 def segment(P: np.ndarray, p: Params):
     """Cuts, then merge, then split: list of inclusive (start, end)."""
-    segs = segments_from_ends(raw_cuts(P, p.delta))
+    if p.seg_fixed > 0:
+        ends = fixed_cuts(P.shape[0], p.seg_fixed)
+    else:
+        ends = raw_cuts(P, p.delta)
+    segs = segments_from_ends(ends)
     segs = merge_short(segs, p.seg_min)
     return split_long(segs, p.seg_max)
 
 
 def segment_capacity(p: Params) -> int:
     """Upper bound on the number of segments a head can produce."""
-    n_thr = len(thresholds(1 << 62, p.delta))
-    cap = n_thr + 1 + (p.T // p.seg_max if p.seg_max > 0 else 0)
+    if p.seg_fixed > 0:
+        n_raw = -(-p.T // p.seg_fixed)
+    else:
+        n_raw = len(thresholds(1 << 62, p.delta)) + 1
+    cap = n_raw + (p.T // p.seg_max if p.seg_max > 0 else 0)
     return max(1, min(cap, p.T))
 
 
@@ -413,6 +434,9 @@ def quotas(segs, v: np.ndarray, p: Params):
     floors alone exceed T_keep the quotas stay at the floors and the select
     step's over-budget repair drops the lowest-scored picks (the page: floors
     hold only when the budget allows).
+    Ablation "no mass-weighted quota" [AMS notes, ablations, Table 7]
+    (quota_mode = QUOTA_UNIFORM): every segment weighs 1 instead of M_i, in the
+    share and in the redistribution order alike (so ties go by index).
     Returns (q, floor, A, M) as int64 arrays (M as Python-int object array).
     """
     T = p.T
@@ -425,7 +449,10 @@ def quotas(segs, v: np.ndarray, p: Params):
     L = np.array([b - a + 1 for a, b in segs], dtype=np.int64)
     Kmk = np.array([int(mk[a:b + 1].sum()) for a, b in segs], dtype=np.int64)
     A = L - Kmk
-    M = [int(np.sum(v[a:b + 1][~mk[a:b + 1]], dtype=np.uint64)) for a, b in segs]
+    if p.quota_mode == QUOTA_UNIFORM:
+        M = [1] * n
+    else:
+        M = [int(np.sum(v[a:b + 1][~mk[a:b + 1]], dtype=np.uint64)) for a, b in segs]
     floor_ = np.minimum(A, np.maximum(0, np.minimum(p.q_min, L) - Kmk))
     F = int(floor_.sum())
     if F > t_keep:
@@ -581,5 +608,79 @@ def event(q, k, v, credit_in, p: Params) -> HeadResult:
     per layer and KV head producing a compact budget-length cache]."""
     u = window_usage(q, k, p)
     res = steps2to5(u.astype(np.float32), k, v, credit_in, p)
+    res.u = u
+    return res
+
+
+# ---------------------------------------------------------------------------
+# Ragged (left-padded) multi-batch events
+# ---------------------------------------------------------------------------
+#
+# In a multi-batch decode the prompts of one batch have different lengths and
+# are left-padded to the longest one; the attention mask M keeps the padding
+# out of the attention scores, and padding that stays in the compressed cache
+# eats its budget [SkipKV notes, observation 1; §4.1 token importance with the
+# mask M; §5 B' = B - Delta_pad].  Reading: a head-event with valid length
+# len holds padding at positions [0, T-len) and real tokens at [T-len, T); the
+# event runs on the real tokens only, exactly as on a cache of length len
+# (padding takes no part in the softmax, the masses, the must-keep set or the
+# budget), and its indices are reported in the padded cache's positions.
+
+def valid_length(p: Params, length: int) -> int:
+    """Valid positions of a left-padded head-event, clamped to [W, T]: the
+    window queries are the last W positions and are always real tokens."""
+    return int(min(max(int(length), p.window), p.T))
+
+
+def _to_absolute(res: HeadResult, off: int, T: int) -> HeadResult:
+    """Re-express a head result computed on positions [off, T) in the padded
+    cache's positions: per-position arrays get zeros on the padding, segments
+    and kept indices move by off (kept keeps its -1 padding)."""
+    def pad(x, dtype):
+        if x is None:
+            return None
+        out = np.zeros(T, dtype=dtype)
+        out[off:] = x
+        return out
+    res.u = pad(res.u, np.float64)
+    res.u32 = pad(res.u32, np.float32)
+    res.score = pad(res.score, np.float32)
+    res.w = pad(res.w, np.uint64)
+    res.v = pad(res.v, np.uint64)
+    res.credit_upd = pad(res.credit_upd, np.uint64)
+    res.segs = [(a + off, b + off) for a, b in res.segs]
+    if res.kept is not None:
+        res.kept = np.where(res.kept >= 0, res.kept + off, -1).astype(np.int64)
+    return res
+
+
+def _ragged_params(p: Params, length: int):
+    Tn = valid_length(p, length)
+    return Tn, p.T - Tn, p.with_(T=Tn, n_prev=min(p.n_prev, Tn))
+
+
+def steps2to5_ragged(u32, k, v, credit_in, p: Params, length: int) -> HeadResult:
+    """Steps 2-5 of a left-padded head-event; u32, k and v span all T
+    positions, credit_in holds the credit of the first n_prev real tokens."""
+    Tn, off, pn = _ragged_params(p, length)
+    ci = None if credit_in is None or pn.n_prev == 0 else np.asarray(credit_in)[: pn.n_prev]
+    res = steps2to5(np.asarray(u32)[off:p.T], np.asarray(k)[off:p.T], np.asarray(v)[off:p.T],
+                    ci, pn)
+    return _to_absolute(res, off, p.T)
+
+
+def window_usage_ragged(q, k, p: Params, length: int) -> np.ndarray:
+    """Step 1 of a left-padded head-event: fp64 usage over all T positions,
+    zero on the padding."""
+    Tn, off, pn = _ragged_params(p, length)
+    u = np.zeros(p.T, dtype=np.float64)
+    u[off:] = window_usage(q, np.asarray(k)[off:p.T], pn)
+    return u
+
+
+def event_ragged(q, k, v, credit_in, p: Params, length: int) -> HeadResult:
+    """Whole event for one left-padded head-event."""
+    u = window_usage_ragged(q, k, p, length)
+    res = steps2to5_ragged(u.astype(np.float32), k, v, credit_in, p, length)
     res.u = u
     return res
