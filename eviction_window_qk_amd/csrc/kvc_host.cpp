@@ -78,6 +78,11 @@ static int derive(const kvc_params* p, Derived* d) {
   if (p->n_prev < 0 || p->n_prev > p->T) return KVC_EINVAL;
   if (!p->ema && p->n_prev != 0) return KVC_EINVAL;
   if (!(p->scale >= 0.0f) || !isfinite(p->scale)) return KVC_EINVAL;
+  if (p->seg_fixed < 0) return KVC_EINVAL;
+  if (p->seg_fixed > 0 && (int64_t(p->T) + p->seg_fixed - 1) / p->seg_fixed > kMaxThresholds + 1)
+    return KVC_EINVAL;
+  if (p->quota_mode != KVC_QUOTA_MASS && p->quota_mode != KVC_QUOTA_UNIFORM) return KVC_EINVAL;
+  if (p->valid_len && (reinterpret_cast<uintptr_t>(p->valid_len) & 3u)) return KVC_EINVAL;
   // Element counts must stay addressable.
   const double elems = double(p->n_heads) * double(p->t_stride) * double(p->head_dim);
   if (elems > 9.0e15) return KVC_EINVAL;
@@ -93,22 +98,25 @@ static int derive(const kvc_params* p, Derived* d) {
   d->seg_min = p->seg_min;
   d->seg_max = p->seg_max;
   d->q_min = p->q_min;
-  // Must-keep: sinks first, the recent suffix shrinks when the budget is short.
-  const int s_keep = p->sinks < p->budget ? (p->sinks < p->T ? p->sinks : p->T)
-                                          : (p->budget < p->T ? p->budget : p->T);
-  int r_keep = p->recent;
-  if (r_keep > p->budget - s_keep) r_keep = p->budget - s_keep;
-  if (r_keep > p->T - s_keep) r_keep = p->T - s_keep;
-  d->s_keep = s_keep;
-  d->r_keep = r_keep;
-  d->t_keep = p->budget - s_keep - r_keep;
+  d->sinks = p->sinks;
+  d->recent = p->recent;
+  const Keep mk = must_keep(p->sinks, p->recent, p->budget, p->T);
+  d->s_keep = mk.s;
+  d->r_keep = mk.r;
+  d->t_keep = mk.t_keep;
   d->pool_h = p->pool_kernel / 2;
   d->pool_mode = p->pool_mode;
   d->head_agg = p->head_agg;
   d->ema = p->ema;
   d->n_prev = p->n_prev;
-  d->n_thr = n_thr;
-  int64_t cap = int64_t(n_thr) + 1 + (p->seg_max > 0 ? p->T / p->seg_max : 0);
+  // Raw cuts before merging: mass thresholds, or every seg_fixed positions.
+  const int n_cut =
+      p->seg_fixed > 0 ? int((int64_t(p->T) + p->seg_fixed - 1) / p->seg_fixed) - 1 : n_thr;
+  d->n_thr = n_cut;
+  d->seg_fixed = p->seg_fixed;
+  d->quota_uniform = p->quota_mode == KVC_QUOTA_UNIFORM ? 1 : 0;
+  d->vlen = p->valid_len;
+  int64_t cap = int64_t(n_cut) + 1 + (p->seg_max > 0 ? p->T / p->seg_max : 0);
   if (cap > p->T) cap = p->T;
   if (cap < 1) cap = 1;
   d->s_cap = int(cap);
@@ -245,7 +253,7 @@ int kvc_mass_segment(const kvc_params* p, const float* u, const uint64_t* credit
       reinterpret_cast<int32_t*>(w + L.seg_q), reinterpret_cast<int32_t*>(w + L.ends),
       hipStream_t(stream)));
   if (rc != KVC_OK) return rc;
-  return d.T <= d.K ? KVC_NOOP : KVC_OK;
+  return (d.T <= d.K && !d.vlen) ? KVC_NOOP : KVC_OK;
 }
 
 int kvc_select(const kvc_params* p, const float* score, const int32_t* seg_start,
@@ -269,7 +277,7 @@ int kvc_select(const kvc_params* p, const float* score, const int32_t* seg_start
   rc = launch_status(launch_select(d, score, seg_start, seg_quota, n_seg, kept,
                                    hipStream_t(stream)));
   if (rc != KVC_OK) return rc;
-  return d.T <= d.K ? KVC_NOOP : KVC_OK;
+  return (d.T <= d.K && !d.vlen) ? KVC_NOOP : KVC_OK;
 }
 
 int kvc_gather_compact(const kvc_params* p, const int32_t* kept, const void* k, const void* v,
@@ -347,7 +355,7 @@ int kvc_compress_event(const kvc_params* p, const void* q_win, const void* k, co
   rc = launch_status(launch_gather(d, kept_out, k, v, cupd, k_out, v_out,
                                    d.ema ? credit_out : nullptr, s));
   if (rc != KVC_OK) return rc;
-  return d.T <= d.K ? KVC_NOOP : KVC_OK;
+  return (d.T <= d.K && !d.vlen) ? KVC_NOOP : KVC_OK;
 }
 
 }  // extern "C"

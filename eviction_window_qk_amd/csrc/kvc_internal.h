@@ -20,13 +20,43 @@ constexpr int kScoreKeysPerWave = 64;  // two 32-key MFMA blocks per wave
 struct Derived {
   int NH, G, D, T, TS, W, K, R;
   int seg_min, seg_max, q_min;
-  int s_keep, r_keep, t_keep;   // S', R', budget left after must-keep
+  int sinks, recent;            // requested must-keep sizes
+  int s_keep, r_keep, t_keep;   // S', R', budget left after must-keep (at length T)
   int pool_h, pool_mode, head_agg, ema, n_prev;
   int n_thr, s_cap;
   float c_log2;                 // softmax scale * log2(e)
   uint64_t eps_q;               // ceil(eps * 2^40)
   double delta, lam, oml, beta, omb;
+  int seg_fixed;                // > 0: fixed-length raw segments (ablation)
+  int quota_uniform;            // 1: every segment weighs 1 in the quotas (ablation)
+  const int32_t* vlen;          // NULL or per-head valid length (device)
 };
+
+// A head-event's real tokens: positions [off, off + T) of the padded cache.
+struct Span {
+  int T, off;
+};
+
+__device__ __forceinline__ Span head_span(const Derived& P, int n) {
+  if (!P.vlen) return Span{P.T, 0};
+  int len = P.vlen[n];
+  len = len < P.W ? P.W : (len > P.T ? P.T : len);
+  return Span{len, P.T - len};
+}
+
+// Must-keep sizes and the budget left for the segments, for a cache of
+// length T: sinks first, the recent suffix shrinks when the budget is short.
+struct Keep {
+  int s, r, t_keep;
+};
+
+__host__ __device__ __forceinline__ Keep must_keep(int sinks, int recent, int K, int T) {
+  const int s = sinks < K ? (sinks < T ? sinks : T) : (K < T ? K : T);
+  int r = recent;
+  if (r > K - s) r = K - s;
+  if (r > T - s) r = T - s;
+  return Keep{s, r, K - s - r};
+}
 
 // Workspace carve-up (byte offsets into the caller's buffer, 256-B aligned).
 struct WsLayout {

@@ -136,11 +136,18 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
     int32_t* __restrict__ seg_q, int32_t* __restrict__ ends) {
   __shared__ Shared sh;
   const int n = blockIdx.x;
-  const int T = P.T;
   const int tid = threadIdx.x;
-  const float* un = u + size_t(n) * T;
-  float* sc = score + size_t(n) * T;
-  uint64_t* vn = vp + size_t(n) * T;
+  // A left-padded head runs on its real tokens [off, off + T) only.
+  const Span sp = head_span(P, n);
+  const int T = sp.T;
+  const Keep mk = P.vlen ? must_keep(P.sinks, P.recent, P.K, T) : Keep{P.s_keep, P.r_keep, P.t_keep};
+  const float* un = u + size_t(n) * P.T + sp.off;
+  float* sc = score + size_t(n) * P.T + sp.off;
+  uint64_t* vn = vp + size_t(n) * P.T + sp.off;
+  for (int t = tid; t < sp.off; t += kThreads) {  // padding: score 0, credit 0
+    score[size_t(n) * P.T + t] = 0.0f;
+    if (P.ema) credit_upd[size_t(n) * P.T + t] = 0;
+  }
 
   // -- step 2a/2b: pooled score and fixed-point usage w = trunc(ubar*2^40)+e
   uint64_t part = 0;
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
 
   // -- step 2c: EMA credit and mixed mass (Q44)
   if (P.ema) {
-    uint64_t* cu = credit_upd + size_t(n) * T;
+    uint64_t* cu = credit_upd + size_t(n) * P.T + sp.off;
     const uint64_t* ci = credit_in ? credit_in + size_t(n) * P.n_prev : nullptr;
     const double wd = double(w_total);
     part = 0;
@@ -225,6 +232,11 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
   // -- step 3b: thresholds theta_k = min(V, ceil(k*Delta*V)), cuts e_k
   int32_t* en = ends + size_t(n) * (P.n_thr + 1);
   for (int kk = tid; kk < P.n_thr; kk += kThreads) {
+    if (P.seg_fixed > 0) {  // ablation: a cut every seg_fixed positions
+      const int64_t e = int64_t(kk + 1) * P.seg_fixed - 1;
+      en[kk] = e < T - 1 ? int(e) : T - 1;  // cuts past the end collapse into T-1
+      continue;
+    }
     const double x = ceil((double(kk + 1) * P.delta) * double(V));
     uint64_t th = uint64_t(x);
     if (th > V) th = V;
@@ -281,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
   const int ns = sh.piece_off[nm];  // <= s_cap by construction
 
   // -- step 3e: per-segment length, must-keep overlap, mass, floor
-  const int s_end = P.s_keep - 1, r_beg = T - P.r_keep;
+  const int s_end = mk.s - 1, r_beg = T - mk.r;
   const size_t so = size_t(n) * P.s_cap;
   int64_t f_part = 0;
   uint64_t m_part = 0;
@@ -311,7 +323,8 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
     int fl = lmin - kmk;
     fl = fl < 0 ? 0 : fl;
     fl = fl < avail ? fl : avail;
-    seg_start[so + s] = start;
+    if (P.quota_uniform) mass = 1;  // ablation: every segment weighs the same
+    seg_start[so + s] = sp.off + start;
     seg_m[so + s] = mass;
     seg_a[so + s] = avail;
     seg_f[so + s] = fl;
@@ -322,10 +335,10 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
   const uint64_t SM = block_sum_u64(m_part, sh);
 
   // -- step 3f/3g: quotas
-  if (F > P.t_keep) {
+  if (F > mk.t_keep) {
     for (int s = tid; s < ns; s += kThreads) seg_q[so + s] = seg_f[so + s];
   } else {
-    const int64_t t_rem = P.t_keep - F;
+    const int64_t t_rem = mk.t_keep - F;
     int64_t q_part = 0;
     for (int s = tid; s < ns; s += kThreads) {
       int64_t add = 0;
@@ -338,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
       seg_q[so + s] = int32_t(qv);
       q_part += qv;
     }
-    const int64_t D = int64_t(P.t_keep) - block_sum_i64(q_part, sh);
+    const int64_t D = int64_t(mk.t_keep) - block_sum_i64(q_part, sh);
     if (D != 0) {
       // Cyclic walk in closed form: c full cycles give every segment
       // min(room, c); the next, partial cycle gives one more to the first r

@@ -204,7 +204,8 @@ __global__ __launch_bounds__(kRsThreads, 3) void k_rowstats(Derived P, const u32
   const int n = lb / groups, grp = lb % groups;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, h = lane >> 5;
-  const int T = P.T, W = P.W, R = P.R;
+  const Span sp = head_span(P, n);  // real tokens of a left-padded head
+  const int T = sp.T, W = P.W, R = P.R;
   const float c = P.c_log2;
 
   RsCtx<D> cx;
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kRsThreads, 3) void k_rowstats(Derived P, const u32
     cx.l[rb] = 0.0f;
   }
 
-  const u32x4* kn = k + size_t(n) * P.TS * kPerRow;
+  const u32x4* kn = k + (size_t(n) * P.TS + sp.off) * kPerRow;
   const int n_tiles = (T + kRsTile - 1) / kRsTile;
   auto fetch = [&](int kt, u32x4 (&pre)[kLoads]) {
 #pragma unroll
@@ -417,7 +418,9 @@ __global__ __launch_bounds__(kCsThreads, SUM ? 3 : 2) void k_colsum(Derived P, c
   const int n = lb / chunks, chunk = lb % chunks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, h = lane >> 5;
-  const int T = P.T, W = P.W, R = P.R, G = P.G;
+  const Span sp = head_span(P, n);  // real tokens of a left-padded head
+  const int T = sp.T, W = P.W, R = P.R, G = P.G;
+  if (chunk * kCsKeys >= T) return;  // whole workgroup: no real key in this chunk
   const float c = P.c_log2;
   const int key_base = chunk * kCsKeys + wave * kScoreKeysPerWave;
 
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(kCsThreads, SUM ? 3 : 2) void k_colsum(Derived P, c
 
   CsCtx<D> cx;
   cx.key0 = key_base + j;
-  const u32x4* kn = k + size_t(n) * P.TS * kPerRow;
+  const u32x4* kn = k + (size_t(n) * P.TS + sp.off) * kPerRow;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     int t = key_base + kb * 32 + j;
@@ -458,18 +461,22 @@ __global__ __launch_bounds__(kCsThreads, SUM ? 3 : 2) void k_colsum(Derived P, c
     cx.cs1 = tot1;
   }
   if (h == 0) {
-    if (key_base + j < T) u[size_t(n) * T + key_base + j] = cx.cs0;
-    if (key_base + 32 + j < T) u[size_t(n) * T + key_base + 32 + j] = cx.cs1;
+    float* un = u + size_t(n) * P.T + sp.off;
+    if (key_base + j < T) un[key_base + j] = cx.cs0;
+    if (key_base + 32 + j < T) un[key_base + 32 + j] = cx.cs1;
   }
 }
 
 // Positions T-W+1 .. T-1 are seen by fewer than W queries: replace them by
-// the maximum usage over the fully observed positions 0 .. T-W.
+// the maximum usage over the fully observed positions 0 .. T-W (positions of
+// the head's real tokens; the padding of a left-padded head gets 0).
 __global__ __launch_bounds__(256) void k_fill(Derived P, float* __restrict__ u) {
   __shared__ float red[4];
   const int n = blockIdx.x;
-  const int T = P.T, W = P.W;
-  float* un = u + size_t(n) * T;
+  const Span sp = head_span(P, n);
+  const int T = sp.T, W = P.W;
+  for (int t = threadIdx.x; t < sp.off; t += 256) u[size_t(n) * P.T + t] = 0.0f;  // padding
+  float* un = u + size_t(n) * P.T + sp.off;
   float m = -INFINITY;
   for (int t = threadIdx.x; t <= T - W; t += 256) m = fmaxf(m, un[t]);
 #pragma unroll

@@ -98,16 +98,20 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
                                                      int32_t* __restrict__ kept) {
   __shared__ Shared sh;
   const int n = blockIdx.x;
-  const int T = P.T, K = P.K;
+  // A left-padded head runs on its real tokens [off, off + T) only; kept
+  // holds positions of the padded cache.
+  const Span sp = head_span(P, n);
+  const int T = sp.T, K = P.K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* kn = kept + size_t(n) * K;
   if (T <= K) {  // nothing to evict: identity, -1 past T
-    for (int j = tid; j < K; j += kThreads) kn[j] = j < T ? j : -1;
+    for (int j = tid; j < K; j += kThreads) kn[j] = j < T ? sp.off + j : -1;
     return;
   }
-  const float* sc = score + size_t(n) * T;
+  const float* sc = score + size_t(n) * P.T + sp.off;
   const int nw = (T + 31) >> 5;
-  const int s_keep = P.s_keep, r_beg = T - P.r_keep;
+  const Keep mk = P.vlen ? must_keep(P.sinks, P.recent, P.K, T) : Keep{P.s_keep, P.r_keep, P.t_keep};
+  const int s_keep = mk.s, r_beg = T - mk.r;
   auto must_keep = [&](int t) { return t < s_keep || t >= r_beg; };
 
   for (int w = tid; w < nw; w += kThreads) sh.bits[w] = 0;
@@ -120,8 +124,8 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
   ns = ns < 0 ? 0 : (ns > P.s_cap ? P.s_cap : ns);
   const int32_t* ss = seg_start + size_t(n) * P.s_cap;
   const int32_t* sq = seg_quota + size_t(n) * P.s_cap;
-  auto seg_bounds = [&](int i, int* a, int* b) {
-    int s0 = ss[i], s1 = i + 1 < ns ? ss[i + 1] : T;
+  auto seg_bounds = [&](int i, int* a, int* b) {  // starts are padded-cache positions
+    int s0 = ss[i] - sp.off, s1 = i + 1 < ns ? ss[i + 1] - sp.off : T;
     s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
     s1 = s1 < 0 ? 0 : (s1 > T ? T : s1);
     *a = s0;
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
   uint32_t c = 0;
   for (int w = tid; w < nw; w += kThreads) c += __popc(sh.bits[w]);
   const uint32_t n_keep = block_count(c, sh);
-  const uint32_t n_mk = uint32_t(s_keep + P.r_keep);
+  const uint32_t n_mk = uint32_t(mk.s + mk.r);
   if (n_keep > uint32_t(K)) {
     // Keep the best K - |MK| picks, drop the rest (the lowest-scored first).
     auto is_pick = [&](int t) { return !must_keep(t) && test_bit(sh, t); };
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
     while (word) {
       const int b = __ffs(word) - 1;
       word &= word - 1;
-      if (pos < uint32_t(K)) kn[pos] = w * 32 + b;
+      if (pos < uint32_t(K)) kn[pos] = sp.off + w * 32 + b;
       ++pos;
     }
   }

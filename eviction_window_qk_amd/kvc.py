@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 OK, NOOP = 0, 1
 POOL_AVG, POOL_MAX = 0, 1
 AGG_SUM, AGG_MAX = 0, 1
+QUOTA_MASS, QUOTA_UNIFORM = 0, 1
 
 
 class KvcError(RuntimeError):
@@ -43,6 +44,8 @@ class _CParams(ctypes.Structure):
         ("head_agg", ctypes.c_int32), ("ema", ctypes.c_int32), ("n_prev", ctypes.c_int32),
         ("scale", ctypes.c_float), ("delta", ctypes.c_double), ("lambda_", ctypes.c_double),
         ("beta", ctypes.c_double), ("eps", ctypes.c_double),
+        ("seg_fixed", ctypes.c_int32), ("quota_mode", ctypes.c_int32),
+        ("valid_len", ctypes.c_void_p),
     ]
 
 
@@ -71,6 +74,9 @@ class Params:
     eps: float = 1e-6
     n_prev: int = 0
     scale: float = 0.0
+    seg_fixed: int = 0         # ablation: > 0 => fixed-length raw segments
+    quota_mode: int = QUOTA_MASS
+    valid_len: object = None   # None or int32 device tensor [n_heads] (left padding)
 
     @classmethod
     def from_dict(cls, d: dict, **over) -> "Params":
@@ -88,6 +94,9 @@ class Params:
                 c.t_stride = int(v) if v else int(self.T)
             elif f.name == "ema":
                 c.ema = 1 if v else 0
+            elif f.name == "valid_len":
+                c.valid_len = None if v is None else _ptr(v, (torch.int32,), (self.n_heads,),
+                                                          "valid_len")
             elif f.name in ("delta", "beta", "eps", "scale"):
                 setattr(c, f.name, float(v))
             else:

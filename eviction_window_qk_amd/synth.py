@@ -209,3 +209,14 @@ def random_small(seed: int, n_heads: int, G: int, W: int, d: int, T: int,
                                 * np.float32(key_scale))
     v[:, :T] = f32_to_bf16_bits(rng.standard_normal((n_heads, T, d), dtype=np.float32))
     return q, k, v
+
+
+def batch_valid_lengths(wl: Workload, max_pad: int, seed: int, heads=None) -> np.ndarray:
+    """Valid lengths of a left-padded batch: batch element b gets a pad count
+    drawn uniformly from 0..max_pad, shared by all its layers and KV heads
+    (the prompts of one batch differ in length, every layer sees the same
+    padding).  Returns int32 [len(heads)] (all heads by default)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, wl.batch, max_pad])))
+    pads = rng.integers(0, max_pad + 1, size=wl.batch)
+    heads = range(wl.n_heads) if heads is None else heads
+    return np.array([wl.T - pads[wl.head_coords(n)[1]] for n in heads], dtype=np.int32)

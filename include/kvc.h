@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 enum kvc_status {
   KVC_OK = 0,
@@ -75,9 +75,11 @@ enum kvc_status {
 
 enum { KVC_POOL_AVG = 0, KVC_POOL_MAX = 1 };
 enum { KVC_AGG_SUM = 0, KVC_AGG_MAX = 1 };
+enum { KVC_QUOTA_MASS = 0, KVC_QUOTA_UNIFORM = 1 };
 
 /* Event parameters, named after the pages' quantities.  Field order fixes the
- * layout: 17 int32, one float, then four doubles (104 bytes, no padding). */
+ * layout: 17 int32, one float, four doubles, two int32, then one pointer
+ * (120 bytes, no padding). */
 typedef struct kvc_params {
   int32_t n_heads;     /* NH independent head-events; 0 = nothing to do      */
   int32_t group;       /* G query heads per KV head, 1..64                   */
@@ -103,6 +105,30 @@ typedef struct kvc_params {
   double lambda;       /* EMA decay, [0,1], e.g. 0.9                          */
   double beta;         /* weight of the current mass, [0,1], e.g. 0.9        */
   double eps;          /* mass floor epsilon, (0, 1], e.g. 1e-6              */
+  int32_t seg_fixed;   /* 0 = cuts from the cumulative mass (the method);
+                          L > 0 = ablation "fixed-length segments" [AMS
+                          notes, ablations, Table 7]: raw segments of L
+                          positions (the last one shorter), then merge and
+                          split as usual; ceil(T/L) <= 1025              */
+  int32_t quota_mode;  /* KVC_QUOTA_MASS (the method) or KVC_QUOTA_UNIFORM:
+                          ablation "no mass-weighted quota" [same table]:
+                          every segment weighs 1 in the share of the
+                          remainder and in the redistribution order      */
+  const int32_t* valid_len; /* NULL, or a DEVICE array [n_heads] for ragged
+                          (left-padded) batches [SkipKV notes, observation 1
+                          and §4.1, attention mask M]: head n holds padding
+                          at positions [0, T-len) and real tokens at
+                          [T-len, T), len = valid_len[n] clamped to [W, T].
+                          The event runs on the real tokens only, exactly
+                          as on a cache of length len: u, score and
+                          credit_upd are 0 on the padding, seg_start and
+                          kept are positions of the padded cache, kept
+                          holds min(budget, len) positions, and
+                          credit_in[n][j] is the credit of position
+                          T-len+j (j < min(n_prev, len)).  With valid_len
+                          set, KVC_NOOP is never returned: a head with
+                          len <= budget gets its identity copy and the
+                          call returns KVC_OK.                            */
 } kvc_params;
 
 /* Step 1: window score [AMS notes, key design 1: usage of the most recent W

@@ -112,10 +112,11 @@ def check_steps2to5(pd: dict, u32: np.ndarray, k_bits: np.ndarray, v_bits: np.nd
 
 
 def check_event_consistency(pd: dict, dq, dk, dv, dci, n_heads: int, n_prev: int = 0,
-                            t_stride: int = 0):
+                            t_stride: int = 0, valid_len=None):
     """kvc_compress_event equals the four stage entry points run in sequence on
     the same arguments, bit for bit, and repeated calls give the same bits."""
     p = kvc_params(pd, n_heads, n_prev, t_stride)
+    p.valid_len = valid_len
     ws = kvc.new_workspace(p, dq.device)
     ev = kvc.compress_event(p, dq, dk, dv, dci, ws=ws, want_u=True)
     ev2 = kvc.compress_event(p, dq, dk, dv, dci, ws=ws, want_u=True)
@@ -177,3 +178,50 @@ def gen_all(name: str, seed=None, T=None, workers: int = 16, chunk: int = 16):
                 print(f"[gen] {name}: {c[-1] + 1}/{wl.n_heads} heads, {time.time() - t0:.1f} s",
                       flush=True)
     return q, k, v
+
+
+def check_steps2to5_ragged(pd: dict, u32: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+                           credit_in, heads, lengths: np.ndarray, n_prev: int = 0):
+    """As check_steps2to5 for a left-padded batch (valid_len set): the listed
+    heads must equal the oracle's ragged steps 2-5 bit for bit, padding
+    included (zeros)."""
+    NH, T = u32.shape
+    dlen = torch.from_numpy(np.ascontiguousarray(lengths, np.int32)).cuda()
+    p = kvc.Params.from_dict(pd, n_heads=NH, n_prev=n_prev, valid_len=dlen)
+    op = oracle_params(pd, n_prev)
+    du = torch.from_numpy(np.ascontiguousarray(u32, np.float32)).cuda()
+    dci = dev_u64(credit_in) if (credit_in is not None and n_prev > 0) else None
+    dk, dv = dev_bf16(k_bits), dev_bf16(v_bits)
+    ws = kvc.new_workspace(p, du.device)
+    ms = kvc.mass_segment(p, du, dci, ws=ws)
+    kept = kvc.select(p, ms["score"], ms["seg_start"], ms["seg_quota"], ms["n_seg"], ws=ws)
+    ko, vo, co = kvc.gather_compact(p, kept, dk, dv, ms.get("credit_upd"))
+    torch.cuda.synchronize()
+    g_score = ms["score"].cpu().numpy()
+    g_nseg, g_start, g_quota = (ms["n_seg"].cpu().numpy(), ms["seg_start"].cpu().numpy(),
+                                ms["seg_quota"].cpu().numpy())
+    g_kept, g_ko, g_vo = kept.cpu().numpy(), host_bits(ko), host_bits(vo)
+    g_cu = host_u64(ms["credit_upd"]) if p.ema else None
+    g_co = host_u64(co) if p.ema else None
+    for n in heads:
+        ci = credit_in[n] if (credit_in is not None and n_prev > 0) else None
+        res = ams.steps2to5_ragged(u32[n], k_bits[n, :T], v_bits[n, :T], ci, op, int(lengths[n]))
+        tag = f"head {n} (len {int(lengths[n])})"
+        np.testing.assert_array_equal(g_score[n].view(np.uint32), res.score.view(np.uint32),
+                                      err_msg=f"{tag}: pooled score")
+        if p.ema:
+            np.testing.assert_array_equal(g_cu[n], res.credit_upd, err_msg=f"{tag}: credit")
+        if res.noop:
+            assert g_nseg[n] == 0, tag
+        else:
+            ns = len(res.segs)
+            assert g_nseg[n] == ns, f"{tag}: {g_nseg[n]} segments, oracle {ns}"
+            np.testing.assert_array_equal(g_start[n, :ns], [a for a, _ in res.segs],
+                                          err_msg=f"{tag}: segment starts")
+            np.testing.assert_array_equal(g_quota[n, :ns], res.q, err_msg=f"{tag}: quotas")
+        np.testing.assert_array_equal(g_kept[n], res.kept, err_msg=f"{tag}: kept")
+        np.testing.assert_array_equal(g_ko[n], res.k_out, err_msg=f"{tag}: K_out")
+        np.testing.assert_array_equal(g_vo[n], res.v_out, err_msg=f"{tag}: V_out")
+        if p.ema:
+            np.testing.assert_array_equal(g_co[n], res.credit_out, err_msg=f"{tag}: credit_out")
+    return dict(kept=g_kept)

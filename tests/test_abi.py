@@ -2,6 +2,7 @@
 include/kvc.h declares, and its host-side validation (pure host code that
 returns before anything is launched) behaves as documented."""
 import ctypes
+import subprocess
 import os
 import re
 
@@ -41,15 +42,31 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert kvc.abi_version() == 1
+    assert kvc.abi_version() == 2
     for code in (0, 1, -1, -2, -3, -4, -5):
         assert kvc.strerror(code) and kvc.strerror(code) != "unknown status"
     assert kvc.strerror(-99) == "unknown status"
 
 
-def test_param_struct_layout():
-    assert ctypes.sizeof(kvc._CParams) == 104
+def test_param_struct_layout(tmp_path):
+    assert ctypes.sizeof(kvc._CParams) == 120
     assert kvc._CParams.delta.offset == 72
+    assert kvc._CParams.valid_len.offset == 112
+    # The binding's field offsets equal the C compiler's for include/kvc.h.
+    names = [f for f, _ in kvc._CParams._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join(
+        f'  printf("%s %zu\\n", "{f}", offsetof(kvc_params, {f.rstrip("_")}));\n' for f in names)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "kvc.h"\nint main(void) {\n'
+                   + body + '  printf("sizeof %zu\\n", sizeof(kvc_params));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(__file__), "..", "include")
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                       text=True).stdout.splitlines())
+    assert int(got["sizeof"]) == ctypes.sizeof(kvc._CParams)
+    for f in names:
+        assert int(got[f]) == getattr(kvc._CParams, f).offset, f
 
 
 def _p(**kw):
@@ -71,6 +88,8 @@ def _p(**kw):
     (dict(n_prev=5), -1),                    # credit without EMA
     (dict(ema=True, n_prev=769), -1), (dict(scale=-1.0), -1), (dict(scale=1e-20), -1),
     (dict(scale=float("inf")), -1),
+    (dict(seg_fixed=-1), -1), (dict(T=4096, seg_fixed=2), -1),  # > 1025 fixed segments
+    (dict(quota_mode=2), -1),
     (dict(window=128, group=64), -1),        # W*G > 4096
     (dict(T=2048, window=512, group=8), -1), # W*G = 4096 but 7*W*W*G >= 2^22
     (dict(n_heads=-1), -1),
