@@ -2,6 +2,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-heads N]
+                    [--ragged MAX_PAD] [--seg-fixed L] [--quota-mode mass|uniform]
+
+--ragged left-pads each batch element's prompt by 0..MAX_PAD positions (its
+real tokens are the last T - pad); --seg-fixed / --quota-mode select the
+fixed-length-segment and uniform-quota ablations.  These variants are
+reported with their own config keys; the headline is the default run.
 
 One step = one compression event over every head-event of the workload
 (all layers x batch x KV heads): window score -> mass/segmentation/quota ->
@@ -68,17 +74,21 @@ def generate(name: str, seed=None, workers: int = 16):
     return q, k, v
 
 
-def algorithmic(wl) -> dict:
+def algorithmic(wl, lengths=None) -> dict:
     """Per-event algorithmic work (one causal QK^T; bytes of the data each
-    stage must move at least once)."""
-    NH, G, W, d, T, K = wl.n_heads, wl.group, wl.window, wl.head_dim, wl.T, wl.budget
-    pairs = W * (T - W) + W * (W + 1) // 2           # causal (query, key) pairs per head
-    flops = 2.0 * d * G * pairs * NH
+    stage must move at least once), summed over the heads' real lengths
+    (all T unless a ragged batch gives per-head lengths)."""
+    G, W, d, K = wl.group, wl.window, wl.head_dim, wl.budget
+    Ts = np.full(wl.n_heads, wl.T, dtype=np.float64) if lengths is None else \
+        np.asarray(lengths, dtype=np.float64)
     ema = bool(wl.params.get("ema"))
-    b_score = NH * (2.0 * T * d + 2.0 * G * W * d + 4.0 * T)
-    b_mass = NH * (4.0 * T + 4.0 * T + (8.0 * K + 16.0 * T if ema else 0.0))
-    b_select = NH * (4.0 * T + 4.0 * K)
-    b_gather = NH * (8.0 * K * d + (16.0 * K if ema else 0.0))
+    pairs = W * (Ts - W) + W * (W + 1) / 2.0         # causal (query, key) pairs per head
+    kk = np.minimum(Ts, K)
+    flops = float(np.sum(2.0 * d * G * pairs))
+    b_score = float(np.sum(2.0 * Ts * d + 2.0 * G * W * d + 4.0 * Ts))
+    b_mass = float(np.sum(4.0 * Ts + 4.0 * Ts + (8.0 * K + 16.0 * Ts if ema else 0.0)))
+    b_select = float(np.sum(4.0 * Ts + 4.0 * K))
+    b_gather = float(np.sum(8.0 * kk * d + (16.0 * kk if ema else 0.0)))
     return dict(flops=flops, b_score=b_score, b_mass=b_mass, b_select=b_select,
                 b_gather=b_gather, b_total=b_score + b_mass + b_select + b_gather)
 
@@ -147,6 +157,12 @@ def main():
                     help="head-events in the CPU oracle sample (default: two whole events)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--ragged", type=int, default=0, metavar="MAX_PAD",
+                    help="left-pad each batch element by 0..MAX_PAD positions (ragged batch)")
+    ap.add_argument("--seg-fixed", type=int, default=0, metavar="L",
+                    help="ablation: fixed-length raw segments of L positions")
+    ap.add_argument("--quota-mode", choices=("mass", "uniform"), default="mass",
+                    help="ablation: uniform instead of mass-weighted quotas")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (the event is independent per head "
@@ -182,7 +198,16 @@ def main():
     del q, k, v
     ema = bool(wl.params.get("ema"))
     n_prev = wl.budget if ema else 0
-    p = kvc.Params.from_dict(wl.event_params(), n_heads=wl.n_heads, n_prev=n_prev)
+    variant = {}
+    if args.seg_fixed:
+        variant["seg_fixed"] = args.seg_fixed
+    if args.quota_mode == "uniform":
+        variant["quota_mode"] = kvc.QUOTA_UNIFORM
+    p = kvc.Params.from_dict(wl.event_params(**variant), n_heads=wl.n_heads, n_prev=n_prev)
+    lengths = None
+    if args.ragged:
+        lengths = synth.batch_valid_lengths(wl, args.ragged, seed=wl.seed)
+        p.valid_len = torch.from_numpy(lengths).to(dev)
     credit = None
     if ema:  # carried credit from a prior event: uniform mass over the kept slots
         credit = torch.full((wl.n_heads, n_prev), (1 << 44) // n_prev, dtype=torch.int64,
@@ -256,8 +281,8 @@ def main():
     stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])
     stage_ms = stage.mean(axis=0)
 
-    alg = algorithmic(wl)
-    tokens = wl.n_heads * wl.T
+    alg = algorithmic(wl, lengths)
+    tokens = wl.n_heads * wl.T if lengths is None else int(lengths.sum())
     achieved = alg["flops"] / (score_ms * 1e-3) / 1e12
     t_roof = max(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12), alg["b_total"] / (PEAK_HBM_GBS * 1e9))
     gather_gbs = alg["b_gather"] / (stage_ms[3] * 1e-3) / 1e9
@@ -277,10 +302,12 @@ def main():
         "config": {"workload": wl.name, "n_heads": wl.n_heads, "layers": wl.layers,
                    "batch": wl.batch, "kv_heads": wl.kv_heads, "group": wl.group,
                    "head_dim": wl.head_dim, "T": wl.T, "window": wl.window,
-                   "budget": wl.budget, "ema": ema, "seed": wl.seed},
+                   "budget": wl.budget, "ema": ema, "seed": wl.seed, **variant,
+                   **({"ragged_max_pad": args.ragged, "real_tokens": tokens} if args.ragged
+                      else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": recorded_traffic(wl.name),
+                     "traffic": None if (args.ragged or variant) else recorded_traffic(wl.name),
                      "kernel": "score stage (k_rowstats + k_colsum + k_fill)",
                      "algorithmic_flops_per_launch": alg["flops"]},
         "events_per_s": 1000.0 / ms,
@@ -290,7 +317,7 @@ def main():
                       "select": stage_ms[2], "gather": stage_ms[3]},
         "gather": {"achieved_GBs": gather_gbs, "frac": gather_gbs / PEAK_HBM_GBS},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not (args.ragged or variant):
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_heads or 2 * wl.n_heads, cores)
     print(json.dumps(line), flush=True)

@@ -142,3 +142,68 @@ def test_full_llama8b_t128k():
     q, k, v = gen_all(name, chunk=4)
     ev = _check_event(name, synth.WORKLOADS[name].event_params(), q, k, v, None, 0, [0, 200], name)
     assert int(ev["kept"].shape[1]) == 4096
+
+
+def test_full_qwen7b_t768_fixed_uniform():
+    """The two quota/segment ablations together at full size (the bench's
+    --seg-fixed 64 --quota-mode uniform run)."""
+    name = "qwen7b_t768"
+    q, k, v = gen_all(name)
+    pd = synth.WORKLOADS[name].event_params(seg_fixed=64, quota_mode=ams.QUOTA_UNIFORM)
+    _check_event(name, pd, q, k, v, None, 0, [0, 999, 1791], "qwen7b_t768 fixed64+uniform")
+
+
+def test_full_qwen7b_t768_ragged():
+    """A left-padded batch at full size (the bench's --ragged 400 run): each
+    batch element's prompt is shorter by 0..400 tokens."""
+    name = "qwen7b_t768"
+    wl = synth.WORKLOADS[name]
+    pd = wl.event_params()
+    T, K = wl.T, wl.budget
+    q, k, v = gen_all(name)
+    lengths = synth.batch_valid_lengths(wl, 400, seed=wl.seed)
+    heads = [0, 5, 1000, 1791]
+    print(f"[full] ragged {name}: lengths {lengths.min()}..{lengths.max()}, heads {heads}",
+          flush=True)
+    dlen = torch.from_numpy(lengths).cuda()
+    p = kvc_params(pd, wl.n_heads)
+    p.valid_len = dlen
+    dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    ws = kvc.new_workspace(p, dq.device)
+    ev = kvc.compress_event(p, dq, dk, dv, None, ws=ws, want_u=True)
+    torch.cuda.synchronize()
+    kept = ev["kept"].cpu().numpy()
+    for n in range(wl.n_heads):  # properties on every head-event
+        L = int(lengths[n])
+        row = kept[n][kept[n] >= 0]
+        assert len(row) == min(K, L), n
+        assert row[0] >= T - L and row[-1] < T and np.all(np.diff(row) > 0), n
+    idx = ev["kept"].long().clamp(min=0)
+    gk = torch.gather(dk.view(torch.int16), 1, idx[:, :, None].expand(-1, -1, dk.shape[2]))
+    assert torch.equal(gk, ev["k_out"].view(torch.int16)), "K_out rows != K[kept]"
+    u2 = kvc.score_window(p, dq, dk, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(u2.view(torch.int32), ev["u"].view(torch.int32))
+    op = oracle_params(pd)
+    u_gpu = ev["u"].cpu().numpy()
+    u_mix = ev["u"].clone()
+    for n in heads:
+        u_ref = ams.window_usage_ragged(widen(q[n]), widen(k[n]), op, int(lengths[n]))
+        assert_usage_close(u_gpu[n], u_ref, f"ragged head {n}")
+        u_mix[n] = torch.from_numpy(u_ref.astype(np.float32)).cuda()
+    ms = kvc.mass_segment(p, u_mix, None, ws=ws)
+    kept2 = kvc.select(p, ms["score"], ms["seg_start"], ms["seg_quota"], ms["n_seg"], ws=ws)
+    ko, vo, _ = kvc.gather_compact(p, kept2, dk, dv, None)
+    torch.cuda.synchronize()
+    for n in heads:
+        res = ams.steps2to5_ragged(u_mix[n].cpu().numpy(), k[n], v[n], None, op, int(lengths[n]))
+        np.testing.assert_array_equal(ms["score"][n].cpu().numpy().view(np.uint32),
+                                      res.score.view(np.uint32), err_msg=f"head {n} score")
+        ns = len(res.segs)
+        assert int(ms["n_seg"][n]) == ns, f"head {n}"
+        np.testing.assert_array_equal(ms["seg_start"][n, :ns].cpu().numpy(), [a for a, _ in res.segs])
+        np.testing.assert_array_equal(ms["seg_quota"][n, :ns].cpu().numpy(), res.q)
+        np.testing.assert_array_equal(kept2[n].cpu().numpy(), res.kept, err_msg=f"head {n} kept")
+        np.testing.assert_array_equal(host_bits(ko[n]), res.k_out, err_msg=f"head {n} K_out")
+        np.testing.assert_array_equal(host_bits(vo[n]), res.v_out, err_msg=f"head {n} V_out")
+    print(f"[full] ragged {name}: sampled heads bit-exact", flush=True)
