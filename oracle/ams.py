@@ -684,3 +684,48 @@ def event_ragged(q, k, v, credit_in, p: Params, length: int) -> HeadResult:
     res = steps2to5_ragged(u.astype(np.float32), k, v, credit_in, p, length)
     res.u = u
     return res
+
+
+# ---------------------------------------------------------------------------
+# Paged-KV compaction
+# ---------------------------------------------------------------------------
+#
+# [AMS notes, key design 4, appendix E paragraph] The selection is separate
+# from the paged storage layout: the runtime allocates new blocks, copies each
+# head's KV from its kept original positions into the new physical slots, swaps
+# the request's block table and frees the old blocks.  One compacted slot may
+# hold KV from different original positions in different heads.  Layout read
+# here: a pool of blocks [n_blocks][kv_heads][block_size][d]; logical position t
+# of sequence b lives in block table[b][t // block_size], slot t % block_size.
+
+def gather_paged(kept: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                 table_in: np.ndarray, table_out: np.ndarray, kv_heads: int):
+    """Compacted copy into new blocks of the same pools.
+
+    kept [B*kv_heads][K] (-1 = empty slot), head n = b*kv_heads + h; returns new
+    pools where slot j of sequence b's compacted cache (block table_out[b][j //
+    bs], slot j % bs) holds, for head h, the row of logical position
+    kept[n][j] (zeros for -1); blocks not named in table_out are unchanged."""
+    n_blocks, H, bs, d = k_pool.shape
+    assert H == kv_heads
+    k_new, v_new = k_pool.copy(), v_pool.copy()
+    NH, K = kept.shape
+    for n in range(NH):
+        b, h = divmod(n, kv_heads)
+        for j in range(K):
+            dst = int(table_out[b][j // bs]), j % bs
+            t = int(kept[n][j])
+            if t < 0:
+                k_new[dst[0], h, dst[1]] = 0
+                v_new[dst[0], h, dst[1]] = 0
+                continue
+            src = int(table_in[b][t // bs]), t % bs
+            k_new[dst[0], h, dst[1]] = k_pool[src[0], h, src[1]]
+            v_new[dst[0], h, dst[1]] = v_pool[src[0], h, src[1]]
+    return k_new, v_new
+
+
+def read_paged(pool: np.ndarray, table: np.ndarray, b: int, h: int, length: int) -> np.ndarray:
+    """Logical rows 0..length-1 of head h of sequence b through its block table."""
+    bs = pool.shape[2]
+    return np.stack([pool[int(table[b][t // bs]), h, t % bs] for t in range(length)])
