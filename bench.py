@@ -163,6 +163,9 @@ def main():
                     help="ablation: fixed-length raw segments of L positions")
     ap.add_argument("--quota-mode", choices=("mass", "uniform"), default="mass",
                     help="ablation: uniform instead of mass-weighted quotas")
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
+                    help="also time the paged compaction (kvc_gather_paged) with BLOCK-token "
+                         "blocks of a shuffled pool, driven by the event's kept indices")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (the event is independent per head "
@@ -281,6 +284,32 @@ def main():
     stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])
     stage_ms = stage.mean(axis=0)
 
+    paged = None
+    if args.paged:
+        # The same cache as a pool of BLOCK-token blocks [n_blocks, kv_heads, BLOCK, d] in
+        # shuffled order; every (layer, batch) pair is one sequence of the pool.
+        bs, H = args.paged, wl.kv_heads
+        if wl.T % bs or wl.budget % bs:
+            sys.exit("bench.py: --paged needs T and budget multiples of BLOCK")
+        nseq, nb_in, nb_out = wl.n_heads // H, wl.T // bs, wl.budget // bs
+        n_blocks = nseq * (nb_in + nb_out)
+        g = torch.Generator().manual_seed(wl.seed)
+        perm = torch.randperm(n_blocks, generator=g).to(torch.int32)
+        t_in = perm[:nseq * nb_in].view(nseq, nb_in).to(dev)
+        t_out = perm[nseq * nb_in:].contiguous().view(nseq, nb_out).to(dev)
+        k_pool = torch.empty((n_blocks, H, bs, wl.head_dim), dtype=torch.bfloat16, device=dev)
+        v_pool = torch.empty_like(k_pool)
+        blocked = lambda x: x.view(nseq, H, nb_in, bs, wl.head_dim).permute(0, 2, 1, 3, 4) \
+            .reshape(nseq * nb_in, H, bs, wl.head_dim)
+        k_pool[t_in.flatten().long()] = blocked(dk)
+        v_pool[t_in.flatten().long()] = blocked(dv)
+        gp = lambda: kvc.gather_paged(p, kept, k_pool, v_pool, t_in, t_out, H, stream=stream)
+        for _ in range(2):
+            gp()
+        gp_ms = timed(gp, args.steps)
+        b_gp = algorithmic(wl, lengths)["b_gather"]
+        paged = {"block": bs, "ms": gp_ms, "achieved_GBs": b_gp / (gp_ms * 1e-3) / 1e9,
+                 "frac": b_gp / (gp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     alg = algorithmic(wl, lengths)
     tokens = wl.n_heads * wl.T if lengths is None else int(lengths.sum())
     achieved = alg["flops"] / (score_ms * 1e-3) / 1e12
@@ -317,6 +346,8 @@ def main():
                       "select": stage_ms[2], "gather": stage_ms[3]},
         "gather": {"achieved_GBs": gather_gbs, "frac": gather_gbs / PEAK_HBM_GBS},
     }
+    if paged:
+        line["paged_gather"] = paged
     if not args.no_cpu_baseline and not (args.ragged or variant):
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_heads or 2 * wl.n_heads, cores)

@@ -71,7 +71,92 @@ __global__ __launch_bounds__(kThreads) void k_gather_credit(Derived P,
   }
 }
 
+// Paged variant [AMS notes, key design 4, appendix E paragraph]: the runtime
+// gives every sequence newly allocated blocks; the rows of each head are
+// copied from the kept original positions (through the old block table) into
+// consecutive slots of the new blocks.  Pools are [n_blocks][H][bs][D]; head n
+// = b * H + h.  Block ids outside [0, n_blocks) are never dereferenced: a bad
+// destination is skipped, a bad source gives a zero row.  Same thread mapping
+// as k_gather: kUnroll pieces a grid apart, so a thread's loads come from
+// unrelated rows and many table lookups are in flight at once.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_gather_paged(
+    Derived P, const int32_t* __restrict__ kept, const u32x4* __restrict__ k,
+    const u32x4* __restrict__ v, const int32_t* __restrict__ tin, int tin_blocks,
+    const int32_t* __restrict__ tout, int tout_blocks, int H, int bs, int64_t n_blocks,
+    u32x4* __restrict__ k_out, u32x4* __restrict__ v_out, size_t total) {
+  constexpr int kPieces = D / 8;
+  const size_t stride = size_t(gridDim.x) * kThreads;
+  for (size_t base = size_t(blockIdx.x) * kThreads + threadIdx.x; base < total;
+       base += stride * kUnroll) {
+    u32x4 kv[kUnroll], vv[kUnroll];
+    int64_t dst[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const size_t idx = base + i * stride;
+      kv[i] = vv[i] = u32x4{0, 0, 0, 0};
+      dst[i] = -1;
+      if (idx < total) {
+        const size_t row = idx / kPieces;  // n * K + j
+        const int piece = int(idx % kPieces);
+        const int n = int(row / P.K), j = int(row % P.K);
+        const int b = n / H, h = n % H;
+        const int64_t db = tout[size_t(b) * tout_blocks + j / bs];
+        if (db >= 0 && db < n_blocks)
+          dst[i] = ((db * H + h) * bs + j % bs) * kPieces + piece;
+        const int t = kept[row];
+        if (t >= 0 && t < P.T) {
+          const int64_t sb = tin[size_t(b) * tin_blocks + t / bs];
+          if (sb >= 0 && sb < n_blocks) {
+            const int64_t src = ((sb * H + h) * bs + t % bs) * kPieces + piece;
+            kv[i] = k[src];
+            vv[i] = v[src];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      if (dst[i] >= 0) {
+        k_out[dst[i]] = kv[i];
+        v_out[dst[i]] = vv[i];
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_paged(const Derived& d, const int32_t* kept, const void* k_pool,
+                               const void* v_pool, const int32_t* table_in, int table_in_blocks,
+                               const int32_t* table_out, int table_out_blocks, int kv_heads,
+                               int block_size, int64_t n_blocks, void* k_pool_out,
+                               void* v_pool_out, const uint64_t* credit_upd,
+                               uint64_t* credit_out, hipStream_t s) {
+  const size_t rows = size_t(d.NH) * d.K;
+  const size_t total = rows * size_t(d.D / 8);
+  size_t blocks = (total + size_t(kThreads) * kUnroll - 1) / (size_t(kThreads) * kUnroll);
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  const u32x4* kk = static_cast<const u32x4*>(k_pool);
+  const u32x4* vv = static_cast<const u32x4*>(v_pool);
+  u32x4* ko = static_cast<u32x4*>(k_pool_out);
+  u32x4* vo = static_cast<u32x4*>(v_pool_out);
+  if (d.D == 128)
+    k_gather_paged<128><<<unsigned(blocks), kThreads, 0, s>>>(
+        d, kept, kk, vv, table_in, table_in_blocks, table_out, table_out_blocks, kv_heads,
+        block_size, n_blocks, ko, vo, total);
+  else
+    k_gather_paged<64><<<unsigned(blocks), kThreads, 0, s>>>(
+        d, kept, kk, vv, table_in, table_in_blocks, table_out, table_out_blocks, kv_heads,
+        block_size, n_blocks, ko, vo, total);
+  if (credit_upd && credit_out) {
+    size_t cb = (rows + kThreads - 1) / kThreads;
+    if (cb > 65536) cb = 65536;
+    k_gather_credit<<<unsigned(cb), kThreads, 0, s>>>(d, kept, credit_upd, credit_out);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const Derived& d, const int32_t* kept, const void* k, const void* v,
                          const uint64_t* credit_upd, void* k_out, void* v_out,

@@ -302,6 +302,47 @@ int kvc_gather_compact(const kvc_params* p, const int32_t* kept, const void* k, 
       launch_gather(d, kept, k, v, credit_upd, k_out, v_out, credit_out, hipStream_t(stream)));
 }
 
+int kvc_gather_paged(const kvc_params* p, int32_t kv_heads, int32_t block_size, int64_t n_blocks,
+                     const int32_t* kept, const void* k_pool, const void* v_pool,
+                     const int32_t* table_in, int32_t table_in_blocks, const int32_t* table_out,
+                     int32_t table_out_blocks, void* k_pool_out, void* v_pool_out,
+                     const uint64_t* credit_upd, uint64_t* credit_out, void* stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != KVC_OK) return rc;
+  if (d.NH == 0) return KVC_OK;
+  if (kv_heads < 1 || d.NH % kv_heads != 0 || block_size < 1 || n_blocks < 1) return KVC_EINVAL;
+  if (int64_t(table_in_blocks) * block_size < d.T) return KVC_EINVAL;
+  if (int64_t(table_out_blocks) * block_size < d.K) return KVC_EINVAL;
+  if (!kept || !k_pool || !v_pool || !table_in || !table_out || !k_pool_out || !v_pool_out)
+    return KVC_EINVAL;
+  if ((credit_upd == nullptr) != (credit_out == nullptr)) return KVC_EINVAL;
+  if (!aligned(kept, 4) || !aligned(table_in, 4) || !aligned(table_out, 4) ||
+      !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_pool_out, 16) ||
+      !aligned(v_pool_out, 16) || (credit_upd && !aligned(credit_upd, 8)) ||
+      (credit_out && !aligned(credit_out, 8)))
+    return KVC_EALIGN;
+  const double pool_elems = double(n_blocks) * kv_heads * block_size * d.D;
+  if (pool_elems > 9.0e15) return KVC_EINVAL;
+  const size_t nh = size_t(d.NH), K = size_t(d.K), B = nh / size_t(kv_heads);
+  const size_t pool = size_t(n_blocks) * size_t(kv_heads) * size_t(block_size) * d.D * 2;
+  // The destination pools may be the source pools (new blocks of the same
+  // allocation); the index arrays and credit must not overlap any pool.
+  const Range in[] = {{kept, nh * K * 4},
+                      {table_in, B * size_t(table_in_blocks) * 4},
+                      {table_out, B * size_t(table_out_blocks) * 4},
+                      {credit_upd, nh * d.T * 8}};
+  const Range out[] = {{k_pool_out, pool}, {v_pool_out, pool}, {credit_out, nh * K * 8}};
+  if (any_alias(in, 4, out, 3)) return KVC_EINVAL;
+  const Range kv_in[] = {{k_pool, pool}, {v_pool, pool}};
+  const Range cred_out[] = {{credit_out, nh * K * 8}};
+  if (any_alias(kv_in, 2, cred_out, 1)) return KVC_EINVAL;
+  if (k_pool_out == v_pool_out) return KVC_EINVAL;
+  return launch_status(launch_gather_paged(
+      d, kept, k_pool, v_pool, table_in, table_in_blocks, table_out, table_out_blocks, kv_heads,
+      block_size, n_blocks, k_pool_out, v_pool_out, credit_upd, credit_out, hipStream_t(stream)));
+}
+
 int kvc_compress_event(const kvc_params* p, const void* q_win, const void* k, const void* v,
                        const uint64_t* credit_in, void* k_out, void* v_out, uint64_t* credit_out,
                        int32_t* kept_out, float* u_out, void* ws, size_t ws_bytes, void* stream) {

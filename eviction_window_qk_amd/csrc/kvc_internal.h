@@ -79,5 +79,11 @@ hipError_t launch_select(const Derived& d, const float* score, const int32_t* se
 hipError_t launch_gather(const Derived& d, const int32_t* kept, const void* k, const void* v,
                          const uint64_t* credit_upd, void* k_out, void* v_out,
                          uint64_t* credit_out, hipStream_t s);
+hipError_t launch_gather_paged(const Derived& d, const int32_t* kept, const void* k_pool,
+                               const void* v_pool, const int32_t* table_in, int table_in_blocks,
+                               const int32_t* table_out, int table_out_blocks, int kv_heads,
+                               int block_size, int64_t n_blocks, void* k_pool_out,
+                               void* v_pool_out, const uint64_t* credit_upd,
+                               uint64_t* credit_out, hipStream_t s);
 
 }  // namespace kvc

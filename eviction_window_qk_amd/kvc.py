@@ -127,6 +127,8 @@ def lib() -> ctypes.CDLL:
         "kvc_mass_segment": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "kvc_select": [P, vp, vp, vp, vp, vp, vp, sz, vp],
         "kvc_gather_compact": [P, vp, vp, vp, vp, vp, vp, vp, vp],
+        "kvc_gather_paged": [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, vp, vp, vp, vp,
+                             ctypes.c_int32, vp, ctypes.c_int32, vp, vp, vp, vp, vp],
         "kvc_compress_event": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "kvc_workspace_bytes": [P],
         "kvc_segment_capacity": [P],
@@ -314,6 +316,37 @@ def gather_compact(p: Params, kept, k, v, credit_upd=None, k_out=None, v_out=Non
         _ptr(credit_out, (torch.int64,), (p.n_heads, p.budget), "credit_out"), _stream(stream))
     _check(rc, "kvc_gather_compact")
     return k_out, v_out, credit_out
+
+
+def gather_paged(p: Params, kept, k_pool, v_pool, table_in, table_out, kv_heads: int,
+                 k_pool_out=None, v_pool_out=None, credit_upd=None, credit_out=None,
+                 stream=None):
+    """Step 5 on a paged cache: pools [n_blocks, kv_heads, block_size, d],
+    tables int32 [B, blocks].  Writes the compacted rows into the blocks of
+    table_out of k_pool_out / v_pool_out (default: the source pools
+    themselves).  Returns (k_pool_out, v_pool_out, credit_out)."""
+    dev = _device(kept)
+    n_blocks, H, bs, d = k_pool.shape
+    B = p.n_heads // kv_heads
+    k_pool_out = k_pool if k_pool_out is None else k_pool_out
+    v_pool_out = v_pool if v_pool_out is None else v_pool_out
+    if credit_upd is not None and credit_out is None:
+        credit_out = torch.empty((p.n_heads, p.budget), dtype=torch.int64, device=dev)
+    pshape = (n_blocks, kv_heads, bs, p.head_dim)
+    c = p.to_c()
+    rc = lib().kvc_gather_paged(
+        ctypes.byref(c), kv_heads, bs, n_blocks,
+        _ptr(kept, (torch.int32,), (p.n_heads, p.budget), "kept"),
+        _ptr(k_pool, _BF16_LIKE, pshape, "k_pool"), _ptr(v_pool, _BF16_LIKE, pshape, "v_pool"),
+        _ptr(table_in, (torch.int32,), (B, table_in.shape[1]), "table_in"), table_in.shape[1],
+        _ptr(table_out, (torch.int32,), (B, table_out.shape[1]), "table_out"),
+        table_out.shape[1],
+        _ptr(k_pool_out, _BF16_LIKE, pshape, "k_pool_out"),
+        _ptr(v_pool_out, _BF16_LIKE, pshape, "v_pool_out"),
+        _ptr(credit_upd, (torch.int64,), (p.n_heads, p.T), "credit_upd"),
+        _ptr(credit_out, (torch.int64,), (p.n_heads, p.budget), "credit_out"), _stream(stream))
+    _check(rc, "kvc_gather_paged")
+    return k_pool_out, v_pool_out, credit_out
 
 
 def compress_event(p: Params, q, k, v, credit_in=None, ws=None, out=None, want_u=False,

@@ -183,6 +183,32 @@ int kvc_gather_compact(const kvc_params* p, const int32_t* kept, const void* k, 
                        const uint64_t* credit_upd, void* k_out, void* v_out,
                        uint64_t* credit_out, void* stream);
 
+/* Step 5 on a paged cache [AMS notes, key design 4, appendix E paragraph:
+ * the runtime allocates new blocks, copies each head's KV from its kept
+ * original positions into the new physical slots, swaps the request's block
+ * table and frees the old blocks; one compacted slot may hold KV from
+ * different original positions in different heads].
+ * Pools: k_pool, v_pool (source) and k_pool_out, v_pool_out (destination,
+ * may be the same allocations) are bf16 [n_blocks][kv_heads][block_size][d].
+ * Head n = b * kv_heads + h (n_heads = B * kv_heads); logical position t of
+ * sequence b lives in block table_in[b][t / block_size], slot t % block_size
+ * (table_in is i32 [B][table_in_blocks], table_in_blocks >= ceil(T /
+ * block_size)).  Slot j of the compacted cache goes to block
+ * table_out[b][j / block_size], slot j % block_size (i32 [B][table_out_blocks],
+ * table_out_blocks >= ceil(budget / block_size)): for head h it receives the
+ * row of position kept[n][j], or zeros where kept is -1.  Blocks named in
+ * table_out must not appear in table_in (the copy reads old blocks while
+ * writing new ones); no other block is written.  Block ids outside
+ * [0, n_blocks) are never dereferenced (the destination row is skipped, a bad
+ * source reads as zeros).  credit_upd/credit_out are optional and as in
+ * kvc_gather_compact.  Swapping the tables and freeing the old blocks are the
+ * caller's; nothing here allocates. */
+int kvc_gather_paged(const kvc_params* p, int32_t kv_heads, int32_t block_size, int64_t n_blocks,
+                     const int32_t* kept, const void* k_pool, const void* v_pool,
+                     const int32_t* table_in, int32_t table_in_blocks, const int32_t* table_out,
+                     int32_t table_out_blocks, void* k_pool_out, void* v_pool_out,
+                     const uint64_t* credit_upd, uint64_t* credit_out, void* stream);
+
 /* The whole event, steps 1-5 in one enqueue [AMS notes, overall framework].
  * credit_in/credit_out as above (credit_out required when ema); u_out (may be
  * NULL) receives the step-1 usage.  kept_out receives the kept positions.

@@ -112,11 +112,12 @@ def test_valid_params_for_every_workload():
 
 def test_segment_capacity_matches_oracle_bound():
     for kw in [dict(), dict(seg_max=0), dict(delta=0.25), dict(delta=1.0, seg_max=0),
+               dict(seg_fixed=64), dict(seg_fixed=7, seg_max=0), dict(seg_fixed=1000),
                dict(T=131072, window=128, group=4, budget=4096), dict(T=20, window=4, budget=5,
                                                                     seg_max=2, delta=0.05)]:
         p = _p(**kw)
         o = ams.Params(T=p.T, window=p.window, budget=p.budget, delta=p.delta, seg_min=p.seg_min,
-                       seg_max=p.seg_max)
+                       seg_max=p.seg_max, seg_fixed=p.seg_fixed)
         assert kvc.segment_capacity(p) == ams.segment_capacity(o)
     assert kvc.segment_capacity(_p(T=131072, window=128, group=4, budget=4096)) == 522
 
@@ -195,3 +196,24 @@ def test_binding_rejects_cpu_tensors():
     k = torch.zeros((1, 768, 128), dtype=torch.bfloat16)
     with pytest.raises((ValueError, RuntimeError)):
         kvc.score_window(p, q, k, u=torch.zeros((1, 768)), ws=torch.zeros(8, dtype=torch.uint8))
+
+
+def _call_paged(p, kv_heads=4, bs=16, n_blocks=4096, tin_blocks=48, tout_blocks=16,
+                k_out=FAKE + (5 << 32), v_out=FAKE + (6 << 32)):
+    c = p.to_c()
+    a = FAKE
+    return kvc.lib().kvc_gather_paged(ctypes.byref(c), kv_heads, bs, n_blocks, a,
+                                      a + (1 << 32), a + (2 << 32), a + (3 << 32), tin_blocks,
+                                      a + (4 << 32), tout_blocks, k_out, v_out, None, None, None)
+
+
+def test_gather_paged_validation():
+    p = _p(n_heads=8, T=768, budget=256)          # 2 sequences x 4 KV heads
+    assert _call_paged(p, kv_heads=3) == -1        # n_heads not a multiple of kv_heads
+    assert _call_paged(p, tin_blocks=47) == -1     # 47 * 16 < T
+    assert _call_paged(p, tout_blocks=15) == -1    # 15 * 16 < budget
+    assert _call_paged(p, bs=0) == -1
+    assert _call_paged(p, n_blocks=0) == -1
+    assert _call_paged(p, k_out=FAKE + (4 << 32)) == -1       # output pool overlaps table_out
+    assert _call_paged(p, v_out=FAKE + (5 << 32) + 64) == -1  # the two output pools overlap
+    assert _call_paged(p, k_out=FAKE + (5 << 32) + 8) == -2   # misaligned
