@@ -10,5 +10,7 @@ the seeded input generator module, which holds none of the method's arithmetic.
                  for mass / segmentation / quota / select / gather).
 ``oracle.loops`` pure-Python loop re-statement for tiny shapes, used only to
                  cross-check ``oracle.ams``.
+``oracle.refresh`` the RefreshKV decode-loop pieces around the event (query
+                 comparison trigger, partial-cache append/evict, full-cache sync).
 """
-from . import ams, loops  # noqa: F401
+from . import ams, loops, refresh  # noqa: F401
