@@ -146,6 +146,59 @@ def cpu_baseline(name: str, n_heads: int, cores: int) -> dict:
                       f"{sum(busy):.1f} s of CPU work in {wall:.1f} s wall"}
 
 
+def refresh_pieces(wl, steps: int, warmup: int) -> dict:
+    """Times of the RefreshKV decode-loop pieces at the workload's shape: one
+    query comparison over every (layer, sequence) row, one partial step over
+    every head, and the full sync of 16 decoded tokens per head."""
+    import torch
+    from eviction_window_qk_amd import kvc
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(wl.seed)
+    rows, Hq, d = wl.layers * wl.batch, wl.kv_heads * wl.group, wl.head_dim
+    NH, K, T = wl.n_heads, wl.budget, wl.T
+    q = torch.randn((rows, Hq, d), generator=g).to(torch.bfloat16).to(dev)
+    q_ref = torch.randn((rows, d), generator=g, dtype=torch.float64).to(dev)
+    ps = torch.rand((NH, K), generator=g).to(dev)
+    pp = torch.randint(0, T, (NH, K), generator=g, dtype=torch.int32).to(dev)
+    kp = torch.randn((NH, K, d), generator=g).to(torch.bfloat16).to(dev)
+    vp = torch.randn_like(kp)
+    kn = torch.randn((NH, d), generator=g).to(torch.bfloat16).to(dev)
+    vn = torch.randn_like(kn)
+    kf = torch.zeros((NH, T + 16, d), dtype=torch.bfloat16, device=dev)
+    vf = torch.zeros_like(kf)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1000.0  # us
+
+    t_qc = timed(lambda: kvc.qc_trigger(q, q_ref, 0.5, update_ref=False, stream=stream))
+    t_app = timed(lambda: kvc.partial_append(ps, pp, kp, vp, kn, vn, T, stream=stream))
+    # 16 tokens decoded since the last full step, in random slots of each head
+    pp.copy_(torch.randint(0, T, (NH, K), generator=g, dtype=torch.int32).to(dev))
+    slots = torch.rand((NH, K), generator=g).argsort(dim=1)[:, :16].to(dev)
+    pp.scatter_(1, slots, (T + torch.arange(16, dtype=torch.int32, device=dev)).expand(NH, 16)
+                .contiguous())
+    t_sync = timed(lambda: kvc.full_sync(pp, kp, vp, kf, vf, T, stream=stream))
+    b_qc = rows * Hq * d * 2 + rows * d * 8
+    b_app = NH * K * 4 + NH * (2 * d * 2 * 2 + 8)
+    b_sync = NH * K * 4 + NH * 16 * d * 2 * 2 * 2
+    return {"metric": "RefreshKV decode-loop pieces: us per call", "workload": wl.name,
+            "rows": rows, "heads_q": Hq, "n_heads": NH, "budget": K, "head_dim": d,
+            "qc_trigger_us": t_qc, "partial_append_us": t_app, "full_sync_us": t_sync,
+            "GBs": {"qc_trigger": b_qc / t_qc / 1e3, "partial_append": b_app / t_app / 1e3,
+                    "full_sync": b_sync / t_sync / 1e3},
+            "steps": steps, "warmup": warmup}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +216,9 @@ def main():
                     help="ablation: fixed-length raw segments of L positions")
     ap.add_argument("--quota-mode", choices=("mass", "uniform"), default="mass",
                     help="ablation: uniform instead of mass-weighted quotas")
+    ap.add_argument("--refresh", action="store_true",
+                    help="time the RefreshKV decode-loop pieces (query comparison, partial "
+                         "append/evict, full sync) at the workload's shape instead of the event")
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
                     help="also time the paged compaction (kvc_gather_paged) with BLOCK-token "
                          "blocks of a shuffled pool, driven by the event's kept indices")
@@ -189,6 +245,9 @@ def main():
         print(json.dumps({"copy_probe_bytes": args.copy_probe}))
         return
     wl = synth.WORKLOADS[args.workload]
+    if args.refresh:
+        print(json.dumps(refresh_pieces(wl, args.steps, args.warmup)), flush=True)
+        return
     cores = min(len(os.sched_getaffinity(0)), 16)
     t_gen = time.perf_counter()
     q, k, v = generate(args.workload, workers=cores)

@@ -343,6 +343,80 @@ int kvc_gather_paged(const kvc_params* p, int32_t kv_heads, int32_t block_size, 
       block_size, n_blocks, k_pool_out, v_pool_out, credit_upd, credit_out, hipStream_t(stream)));
 }
 
+int kvc_qc_trigger(int32_t rows, int32_t heads_q, int32_t head_dim, const void* q, double* q_ref,
+                   double threshold, int32_t update_ref, int32_t* full, double* cos_out,
+                   void* stream) {
+  if (rows < 0 || heads_q < 1 || heads_q > 4096 || (head_dim != 64 && head_dim != 128))
+    return KVC_EINVAL;
+  if (!std::isfinite(threshold)) return KVC_EINVAL;
+  if (rows == 0) return KVC_OK;
+  if (!q || !q_ref || !full) return KVC_EINVAL;
+  if (!aligned(q, 2) || !aligned(q_ref, 8) || !aligned(full, 4) || (cos_out && !aligned(cos_out, 8)))
+    return KVC_EALIGN;
+  const size_t r = size_t(rows);
+  const Range in[] = {{q, r * heads_q * head_dim * 2}};
+  const Range out[] = {{q_ref, r * head_dim * 8}, {full, r * 4}, {cos_out, r * 8}};
+  if (any_alias(in, 1, out, 3)) return KVC_EINVAL;
+  return launch_status(launch_qc_trigger(rows, heads_q, head_dim, q, q_ref, threshold,
+                                         update_ref != 0, full, cos_out, hipStream_t(stream)));
+}
+
+int kvc_partial_init(const kvc_params* p, const int32_t* kept, const float* score,
+                     float* part_score, int32_t* part_pos, void* stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != KVC_OK) return rc;
+  if (d.NH == 0) return KVC_OK;
+  if (!kept || !score || !part_score || !part_pos) return KVC_EINVAL;
+  if (!aligned(kept, 4) || !aligned(score, 4) || !aligned(part_score, 4) || !aligned(part_pos, 4))
+    return KVC_EALIGN;
+  const size_t nh = size_t(d.NH), K = size_t(d.K);
+  const Range in[] = {{kept, nh * K * 4}, {score, nh * size_t(d.T) * 4}};
+  const Range out[] = {{part_score, nh * K * 4}, {part_pos, nh * K * 4}};
+  if (any_alias(in, 2, out, 2)) return KVC_EINVAL;
+  return launch_status(launch_partial_init(d.NH, d.K, d.T, kept, score, part_score, part_pos,
+                                           hipStream_t(stream)));
+}
+
+int kvc_partial_append(int32_t n_heads, int32_t K, int32_t head_dim, float* part_score,
+                       int32_t* part_pos, void* k_part, void* v_part, const void* k_new,
+                       const void* v_new, int32_t t_new, int32_t* evicted, void* stream) {
+  if (n_heads < 0 || K < 1 || (head_dim != 64 && head_dim != 128) || t_new < 0) return KVC_EINVAL;
+  if (n_heads == 0) return KVC_OK;
+  if (!part_score || !part_pos || !k_part || !v_part || !k_new || !v_new || !evicted)
+    return KVC_EINVAL;
+  if (!aligned(part_score, 4) || !aligned(part_pos, 4) || !aligned(evicted, 4) ||
+      !aligned(k_part, 16) || !aligned(v_part, 16) || !aligned(k_new, 16) || !aligned(v_new, 16))
+    return KVC_EALIGN;
+  const size_t nh = size_t(n_heads), kk = size_t(K), row = size_t(head_dim) * 2;
+  const Range in[] = {{k_new, nh * row}, {v_new, nh * row}};
+  const Range out[] = {{part_score, nh * kk * 4}, {part_pos, nh * kk * 4}, {k_part, nh * kk * row},
+                       {v_part, nh * kk * row}, {evicted, nh * 4}};
+  if (any_alias(in, 2, out, 5)) return KVC_EINVAL;
+  return launch_status(launch_partial_append(n_heads, K, head_dim, part_score, part_pos, k_part,
+                                             v_part, k_new, v_new, t_new, evicted,
+                                             hipStream_t(stream)));
+}
+
+int kvc_full_sync(int32_t n_heads, int32_t K, int32_t head_dim, const int32_t* part_pos,
+                  const void* k_part, const void* v_part, int32_t t_from, int32_t t_stride,
+                  void* k_full, void* v_full, void* stream) {
+  if (n_heads < 0 || K < 1 || (head_dim != 64 && head_dim != 128) || t_from < 0 || t_stride < 1)
+    return KVC_EINVAL;
+  if (n_heads == 0) return KVC_OK;
+  if (!part_pos || !k_part || !v_part || !k_full || !v_full) return KVC_EINVAL;
+  if (!aligned(part_pos, 4) || !aligned(k_part, 16) || !aligned(v_part, 16) ||
+      !aligned(k_full, 16) || !aligned(v_full, 16))
+    return KVC_EALIGN;
+  const size_t nh = size_t(n_heads), row = size_t(head_dim) * 2;
+  const Range in[] = {{part_pos, nh * size_t(K) * 4}, {k_part, nh * size_t(K) * row},
+                      {v_part, nh * size_t(K) * row}};
+  const Range out[] = {{k_full, nh * size_t(t_stride) * row}, {v_full, nh * size_t(t_stride) * row}};
+  if (any_alias(in, 3, out, 2)) return KVC_EINVAL;
+  return launch_status(launch_full_sync(n_heads, K, head_dim, part_pos, k_part, v_part, t_from,
+                                        t_stride, k_full, v_full, hipStream_t(stream)));
+}
+
 int kvc_compress_event(const kvc_params* p, const void* q_win, const void* k, const void* v,
                        const uint64_t* credit_in, void* k_out, void* v_out, uint64_t* credit_out,
                        int32_t* kept_out, float* u_out, void* ws, size_t ws_bytes, void* stream) {

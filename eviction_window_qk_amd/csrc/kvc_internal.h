@@ -86,4 +86,15 @@ hipError_t launch_gather_paged(const Derived& d, const int32_t* kept, const void
                                void* v_pool_out, const uint64_t* credit_upd,
                                uint64_t* credit_out, hipStream_t s);
 
+hipError_t launch_qc_trigger(int rows, int Hq, int d, const void* q, double* q_ref, double thr,
+                             int update, int32_t* full, double* cos_out, hipStream_t s);
+hipError_t launch_partial_init(int NH, int K, int T, const int32_t* kept, const float* score,
+                               float* ps, int32_t* pp, hipStream_t s);
+hipError_t launch_partial_append(int NH, int K, int d, float* ps, int32_t* pp, void* kp, void* vp,
+                                 const void* kn, const void* vn, int t_new, int32_t* evicted,
+                                 hipStream_t s);
+hipError_t launch_full_sync(int NH, int K, int d, const int32_t* pp, const void* kp,
+                            const void* vp, int t_from, int t_stride, void* kf, void* vf,
+                            hipStream_t s);
+
 }  // namespace kvc

@@ -130,6 +130,13 @@ def lib() -> ctypes.CDLL:
         "kvc_gather_paged": [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, vp, vp, vp, vp,
                              ctypes.c_int32, vp, ctypes.c_int32, vp, vp, vp, vp, vp],
         "kvc_compress_event": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "kvc_qc_trigger": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                           ctypes.c_double, ctypes.c_int32, vp, vp, vp],
+        "kvc_partial_init": [P, vp, vp, vp, vp, vp],
+        "kvc_partial_append": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp,
+                               vp, vp, ctypes.c_int32, vp, vp],
+        "kvc_full_sync": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp,
+                          ctypes.c_int32, ctypes.c_int32, vp, vp, vp],
         "kvc_workspace_bytes": [P],
         "kvc_segment_capacity": [P],
         "kvc_check_params": [P],
@@ -377,3 +384,64 @@ def compress_event(p: Params, q, k, v, credit_in=None, ws=None, out=None, want_u
         ws.numel(), _stream(stream))
     o["status"] = _check(rc, "kvc_compress_event")
     return o
+
+
+# ---------------------------------------------------------------------------
+# RefreshKV decode-loop pieces (include/kvc.h documents each call)
+# ---------------------------------------------------------------------------
+
+def qc_trigger(q, q_ref, threshold: float, update_ref: bool = True, want_cos: bool = False,
+               stream=None):
+    """Query comparison: q bf16 [rows, Hq, d], q_ref float64 [rows, d] (updated in
+    place where a row fires).  Returns full (int32 [rows]) or (full, cos)."""
+    rows, Hq, d = q.shape
+    dev = _device(q)
+    full = torch.empty((rows,), dtype=torch.int32, device=dev)
+    cos = torch.empty((rows,), dtype=torch.float64, device=dev) if want_cos else None
+    rc = lib().kvc_qc_trigger(rows, Hq, d, _ptr(q, _BF16_LIKE, (rows, Hq, d), "q"),
+                              _ptr(q_ref, (torch.float64,), (rows, d), "q_ref"), float(threshold),
+                              1 if update_ref else 0, _ptr(full, (torch.int32,), (rows,), "full"),
+                              _ptr(cos, (torch.float64,), (rows,), "cos"), _stream(stream))
+    _check(rc, "kvc_qc_trigger")
+    return (full, cos) if want_cos else full
+
+
+def partial_init(p: Params, kept, score, stream=None):
+    """C_p bookkeeping after a refresh.  Returns (part_score, part_pos)."""
+    dev = _device(kept)
+    ps = torch.empty((p.n_heads, p.budget), dtype=torch.float32, device=dev)
+    pp = torch.empty((p.n_heads, p.budget), dtype=torch.int32, device=dev)
+    c = p.to_c()
+    rc = lib().kvc_partial_init(ctypes.byref(c),
+                                _ptr(kept, (torch.int32,), (p.n_heads, p.budget), "kept"),
+                                _ptr(score, (torch.float32,), (p.n_heads, p.T), "score"),
+                                ps.data_ptr(), pp.data_ptr(), _stream(stream))
+    _check(rc, "kvc_partial_init")
+    return ps, pp
+
+
+def partial_append(part_score, part_pos, k_part, v_part, k_new, v_new, t_new: int, stream=None):
+    """One partial step for every head (in place).  Returns the evicted slots."""
+    NH, K, d = k_part.shape
+    dev = _device(k_part)
+    ev = torch.empty((NH,), dtype=torch.int32, device=dev)
+    rc = lib().kvc_partial_append(
+        NH, K, d, _ptr(part_score, (torch.float32,), (NH, K), "part_score"),
+        _ptr(part_pos, (torch.int32,), (NH, K), "part_pos"),
+        _ptr(k_part, _BF16_LIKE, (NH, K, d), "k_part"), _ptr(v_part, _BF16_LIKE, (NH, K, d), "v_part"),
+        _ptr(k_new, _BF16_LIKE, (NH, d), "k_new"), _ptr(v_new, _BF16_LIKE, (NH, d), "v_new"),
+        int(t_new), ev.data_ptr(), _stream(stream))
+    _check(rc, "kvc_partial_append")
+    return ev
+
+
+def full_sync(part_pos, k_part, v_part, k_full, v_full, t_from: int, stream=None):
+    """Write the C_p entries decoded since t_from into the full cache (in place)."""
+    NH, K, d = k_part.shape
+    TS = k_full.shape[1]
+    rc = lib().kvc_full_sync(
+        NH, K, d, _ptr(part_pos, (torch.int32,), (NH, K), "part_pos"),
+        _ptr(k_part, _BF16_LIKE, (NH, K, d), "k_part"), _ptr(v_part, _BF16_LIKE, (NH, K, d), "v_part"),
+        int(t_from), TS, _ptr(k_full, _BF16_LIKE, (NH, TS, d), "k_full"),
+        _ptr(v_full, _BF16_LIKE, (NH, TS, d), "v_full"), _stream(stream))
+    _check(rc, "kvc_full_sync")

@@ -209,6 +209,51 @@ int kvc_gather_paged(const kvc_params* p, int32_t kv_heads, int32_t block_size, 
                      int32_t table_out_blocks, void* k_pool_out, void* v_pool_out,
                      const uint64_t* credit_upd, uint64_t* credit_out, void* stream);
 
+/* RefreshKV decode-loop pieces [notes on "RefreshKV: Updating Small KV Cache
+ * During Long-form Generation", A2 method details: a full cache C_f and a
+ * partial cache C_p of K entries per head; every S steps a query comparison
+ * per layer (cosine of the current query averaged over the layer's query
+ * heads against the one of its last full-attention step, full step when
+ * below the threshold s); partial steps append the new token to C_p and drop
+ * the entry with the lowest score of the last full step; a full step first
+ * writes the tokens decoded with C_p into C_f, then refreshes C_p (the
+ * one-segment event on C_f followed by kvc_partial_init)].  The caller runs
+ * the loop and decides when to call what. */
+
+/* Query comparison for `rows` (layer, sequence) rows.  q: bf16
+ * [rows][heads_q][head_dim], the current token's queries (head_dim 64 or
+ * 128).  q_ref: f64 [rows][head_dim], the head sums of each row's last full
+ * step (the cosine is scale-invariant, so sums decide as means do); read,
+ * and where a row fires and update_ref != 0, overwritten with the current
+ * head sum.  full: i32 [rows], 1 where cos < threshold (a zero vector counts
+ * as cos = 1).  cos_out: optional f64 [rows].  fp64 arithmetic. */
+int kvc_qc_trigger(int32_t rows, int32_t heads_q, int32_t head_dim, const void* q, double* q_ref,
+                   double threshold, int32_t update_ref, int32_t* full, double* cos_out,
+                   void* stream);
+
+/* C_p bookkeeping after a refresh: part_pos[n][j] = kept[n][j] and
+ * part_score[n][j] = score[n][kept[n][j]] (+inf where kept is -1), with
+ * kept/score as produced by the event (f32 score [NH][T], i32 kept
+ * [NH][budget]); part_score f32 and part_pos i32 are [NH][budget]. */
+int kvc_partial_init(const kvc_params* p, const int32_t* kept, const float* score,
+                     float* part_score, int32_t* part_pos, void* stream);
+
+/* One partial step for every head: the slot with the lowest part_score
+ * (first slot on ties; scores must not be NaN) receives k_new[n], v_new[n]
+ * (bf16 [n_heads][head_dim]) in k_part, v_part (bf16 [n_heads][K][head_dim]);
+ * its score becomes +inf and its position t_new.  evicted: i32 [n_heads],
+ * the slot used. */
+int kvc_partial_append(int32_t n_heads, int32_t K, int32_t head_dim, float* part_score,
+                       int32_t* part_pos, void* k_part, void* v_part, const void* k_new,
+                       const void* v_new, int32_t t_new, int32_t* evicted, void* stream);
+
+/* Full step, first half: every C_p slot with t_from <= part_pos < t_stride
+ * is copied to row part_pos of k_full, v_full (bf16 [n_heads][t_stride]
+ * [head_dim]); other rows are untouched. */
+int kvc_full_sync(int32_t n_heads, int32_t K, int32_t head_dim, const int32_t* part_pos,
+                  const void* k_part, const void* v_part, int32_t t_from, int32_t t_stride,
+                  void* k_full, void* v_full, void* stream);
+
 /* The whole event, steps 1-5 in one enqueue [AMS notes, overall framework].
  * credit_in/credit_out as above (credit_out required when ema); u_out (may be
  * NULL) receives the step-1 usage.  kept_out receives the kept positions.

@@ -217,3 +217,18 @@ def test_gather_paged_validation():
     assert _call_paged(p, k_out=FAKE + (4 << 32)) == -1       # output pool overlaps table_out
     assert _call_paged(p, v_out=FAKE + (5 << 32) + 64) == -1  # the two output pools overlap
     assert _call_paged(p, k_out=FAKE + (5 << 32) + 8) == -2   # misaligned
+
+
+def test_refresh_pieces_validation():
+    L = kvc.lib()
+    a = FAKE
+    assert L.kvc_qc_trigger(4, 8, 96, a, a + (1 << 32), 0.5, 1, a + (2 << 32), None, None) == -1
+    assert L.kvc_qc_trigger(4, 8, 128, a, a + (1 << 32), float("nan"), 1, a + (2 << 32), None,
+                            None) == -1
+    assert L.kvc_qc_trigger(4, 8, 128, a, a + 8, 0.5, 1, a + (2 << 32), None, None) == -1  # alias
+    assert L.kvc_qc_trigger(0, 8, 128, None, None, 0.5, 1, None, None, None) == 0
+    assert L.kvc_partial_append(4, 0, 128, a, a, a, a, a, a, 7, a, None) == -1
+    assert L.kvc_partial_append(4, 16, 128, a, a + (1 << 32), a + (2 << 32) + 4, a + (3 << 32),
+                                a + (4 << 32), a + (5 << 32), 7, a + (6 << 32), None) == -2
+    assert L.kvc_full_sync(4, 16, 128, a, a + (1 << 32), a + (2 << 32), -1, 100, a + (3 << 32),
+                           a + (4 << 32), None) == -1
