@@ -1,5 +1,6 @@
 // Steps 2 and 3 on gfx950: mass, EMA credit, prefix, cuts, split/merge,
-// must-keep and quotas.  One workgroup per head-event.
+// must-keep and quotas.  One workgroup per head-event (1024 threads for long
+// caches, 256 otherwise).
 //
 // Sources: AMS notes, key design 1 (m_i = (max(u_i,0)+eps)/sum; c <-
 // lambda*c + (1-lambda)*m; m_used = normalize(beta*m + (1-beta)*normalize(c));
@@ -25,18 +26,32 @@
 namespace kvc {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+// Long caches run with 1024 threads per workgroup (one head per CU is then
+// enough to keep the loads in flight); short ones with 256.
+constexpr int kMaxWaves = 16;
 constexpr int kScanItems = 4;
+constexpr int kSweep = 4;          // positions per thread per pooling tile
+constexpr int kMaxHalo = 31;       // pool_kernel <= 63
 constexpr int kMaxMerged = kMaxThresholds + 1;
 
+// LDS of one workgroup of NT threads (sized by NT so that the short-cache
+// variant keeps several workgroups per CU).
+template <int NT>
 struct Shared {
-  uint64_t red_u64[kWaves];
-  int64_t red_i64[kWaves];
+  static constexpr int kRankStage = 2 * NT;  // segments whose walk data fit LDS
+  uint64_t red_u64[kMaxWaves];
+  int64_t red_i64[kMaxWaves];
   int merged_a[kMaxMerged];
   int merged_b[kMaxMerged];
   int piece_off[kMaxMerged + 1];
   int n_merged;
+  union {
+    float tile[NT * kSweep + 2 * kMaxHalo];  // pooling input tile with halo
+    struct {
+      uint64_t m[kRankStage];                // walk order keys (mass)
+      int32_t room[kRankStage];              // steps left per segment
+    } walk;
+  } u;
 };
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
@@ -61,52 +76,58 @@ __device__ __forceinline__ int64_t wave_max_i64(int64_t v) {
 }
 
 // Block-wide reductions: every thread must call them (uniform control flow).
-__device__ uint64_t block_sum_u64(uint64_t v, Shared& sh) {
+template <int NT>
+__device__ uint64_t block_sum_u64(uint64_t v, Shared<NT>& sh) {
   v = wave_sum_u64(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh.red_u64[threadIdx.x >> 6] = v;
   __syncthreads();
   uint64_t s = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) s += sh.red_u64[i];
+  for (int i = 0; i < NT / 64; ++i) s += sh.red_u64[i];
   return s;
 }
 
-__device__ int64_t block_sum_i64(int64_t v, Shared& sh) {
+template <int NT>
+__device__ int64_t block_sum_i64(int64_t v, Shared<NT>& sh) {
   v = wave_sum_i64(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh.red_i64[threadIdx.x >> 6] = v;
   __syncthreads();
   int64_t s = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) s += sh.red_i64[i];
+  for (int i = 0; i < NT / 64; ++i) s += sh.red_i64[i];
   return s;
 }
 
-__device__ int64_t block_max_i64(int64_t v, Shared& sh) {
+template <int NT>
+__device__ int64_t block_max_i64(int64_t v, Shared<NT>& sh) {
   v = wave_max_i64(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh.red_i64[threadIdx.x >> 6] = v;
   __syncthreads();
   int64_t s = sh.red_i64[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) s = sh.red_i64[i] > s ? sh.red_i64[i] : s;
+  for (int i = 1; i < NT / 64; ++i) s = sh.red_i64[i] > s ? sh.red_i64[i] : s;
   return s;
 }
 
 // Pooled usage at t: centred window of 2h+1, in-range neighbours only.
 // Average: fp32 sum in ascending position order from +0.0, one division.
-__device__ __forceinline__ float pooled(const float* __restrict__ un, int T, int t, int h,
-                                        int mode) {
+// `tile` holds positions [t_base - h, ...) of the head (only in-range
+// positions are ever read).
+__device__ __forceinline__ float pooled(const float* __restrict__ tile, int t_base, int T, int t,
+                                        int h, int mode) {
   const int lo = t - h < 0 ? 0 : t - h;
   const int hi = t + h > T - 1 ? T - 1 : t + h;
+  const float* x = tile + (h - t_base);  // x[j] = u[j]
   if (mode == KVC_POOL_MAX) {
-    float m = un[lo];
-    for (int j = lo + 1; j <= hi; ++j) m = fmaxf(m, un[j]);
+    float m = x[lo];
+    for (int j = lo + 1; j <= hi; ++j) m = fmaxf(m, x[j]);
     return m;
   }
   float acc = 0.0f;
-  for (int j = lo; j <= hi; ++j) acc = acc + un[j];
+  for (int j = lo; j <= hi; ++j) acc = acc + x[j];
   return acc / float(hi - lo + 1);
 }
 
@@ -128,13 +149,14 @@ __device__ __forceinline__ bool precedes(uint64_t mx, int x, uint64_t my, int y,
   return mx < my || (mx == my && x > y);
 }
 
-__global__ __launch_bounds__(kThreads) void k_mass_segment(
+template <int NT>
+__global__ __launch_bounds__(NT) void k_mass_segment(
     Derived P, const float* __restrict__ u, const uint64_t* __restrict__ credit_in,
     float* __restrict__ score, uint64_t* __restrict__ credit_upd, uint64_t* __restrict__ vp,
     int32_t* __restrict__ seg_start, int32_t* __restrict__ seg_quota, int32_t* __restrict__ n_seg,
     uint64_t* __restrict__ seg_m, int32_t* __restrict__ seg_a, int32_t* __restrict__ seg_f,
     int32_t* __restrict__ seg_q, int32_t* __restrict__ ends) {
-  __shared__ Shared sh;
+  __shared__ Shared<NT> sh;
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   // A left-padded head runs on its real tokens [off, off + T) only.
@@ -144,22 +166,37 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
   const float* un = u + size_t(n) * P.T + sp.off;
   float* sc = score + size_t(n) * P.T + sp.off;
   uint64_t* vn = vp + size_t(n) * P.T + sp.off;
-  for (int t = tid; t < sp.off; t += kThreads) {  // padding: score 0, credit 0
+  for (int t = tid; t < sp.off; t += NT) {  // padding: score 0, credit 0
     score[size_t(n) * P.T + t] = 0.0f;
     if (P.ema) credit_upd[size_t(n) * P.T + t] = 0;
   }
 
-  // -- step 2a/2b: pooled score and fixed-point usage w = trunc(ubar*2^40)+e
+  // -- step 2a/2b: pooled score and fixed-point usage w = trunc(ubar*2^40)+e,
+  // one tile of NT*kSweep positions (plus the pooling halo) through LDS
   uint64_t part = 0;
-  for (int t = tid; t < T; t += kThreads) {
-    const float ub = pooled(un, T, t, P.pool_h, P.pool_mode);
-    sc[t] = ub;
-    const float nonneg = ub > 0.0f ? ub : 0.0f;
-    const uint64_t w = uint64_t(nonneg * 1099511627776.0f) + P.eps_q;  // exact 2^40 scale
-    vn[t] = w;
-    part += w;
+  const int h = P.pool_h;
+  for (int t_base = 0; t_base < T; t_base += NT * kSweep) {
+    const int span = NT * kSweep + 2 * h;
+    __syncthreads();  // previous tile consumed
+    for (int i = tid; i < span; i += NT) {
+      const int t = t_base - h + i;
+      if (t >= 0 && t < T) sh.u.tile[i] = un[t];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSweep; ++k) {
+      const int t = t_base + k * NT + tid;
+      if (t < T) {
+        const float ub = pooled(sh.u.tile, t_base, T, t, h, P.pool_mode);
+        sc[t] = ub;
+        const float nonneg = ub > 0.0f ? ub : 0.0f;
+        const uint64_t w = uint64_t(nonneg * 1099511627776.0f) + P.eps_q;  // exact 2^40 scale
+        vn[t] = w;
+        part += w;
+      }
+    }
   }
-  const uint64_t w_total = block_sum_u64(part, sh);
+  const uint64_t w_total = block_sum_u64<NT>(part, sh);
 
   // -- step 2c: EMA credit and mixed mass (Q44)
   if (P.ema) {
@@ -167,21 +204,45 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
     const uint64_t* ci = credit_in ? credit_in + size_t(n) * P.n_prev : nullptr;
     const double wd = double(w_total);
     part = 0;
-    for (int t = tid; t < T; t += kThreads) {
-      const double mq = double(vn[t]) / wd;
-      const double c = t < P.n_prev ? double(ci[t]) * 0x1p-44 : floor(mq * 0x1p44) * 0x1p-44;
-      const double c_new = (P.lam * c) + (P.oml * mq);
-      const uint64_t cq = uint64_t(floor(c_new * 0x1p44));
-      cu[t] = cq;
-      part += cq;
+    for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
+      uint64_t w[kSweep], cin[kSweep];
+#pragma unroll
+      for (int k = 0; k < kSweep; ++k) {  // loads first
+        const int t = t0 + k * NT;
+        w[k] = t < T ? vn[t] : 0;
+        cin[k] = t < T && t < P.n_prev ? ci[t] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < kSweep; ++k) {
+        const int t = t0 + k * NT;
+        if (t >= T) continue;
+        const double mq = double(w[k]) / wd;
+        const double c = t < P.n_prev ? double(cin[k]) * 0x1p-44 : floor(mq * 0x1p44) * 0x1p-44;
+        const double c_new = (P.lam * c) + (P.oml * mq);
+        const uint64_t cq = uint64_t(floor(c_new * 0x1p44));
+        cu[t] = cq;
+        part += cq;
+      }
     }
-    const uint64_t c_total = block_sum_u64(part, sh);
+    const uint64_t c_total = block_sum_u64<NT>(part, sh);
     const double cd = double(c_total);
-    for (int t = tid; t < T; t += kThreads) {
-      const double mq = double(vn[t]) / wd;
-      const double nc = c_total ? double(cu[t]) / cd : 0.0;
-      const double mix = (P.beta * mq) + (P.omb * nc);
-      vn[t] = uint64_t(floor(mix * 0x1p44));
+    for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
+      uint64_t w[kSweep], cq[kSweep];
+#pragma unroll
+      for (int k = 0; k < kSweep; ++k) {
+        const int t = t0 + k * NT;
+        w[k] = t < T ? vn[t] : 0;
+        cq[k] = t < T ? cu[t] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < kSweep; ++k) {
+        const int t = t0 + k * NT;
+        if (t >= T) continue;
+        const double mq = double(w[k]) / wd;
+        const double nc = c_total ? double(cq[k]) / cd : 0.0;
+        const double mix = (P.beta * mq) + (P.omb * nc);
+        vn[t] = uint64_t(floor(mix * 0x1p44));
+      }
     }
   }
 
@@ -196,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
   {
     uint64_t carry = 0;
     const int lane = tid & 63, wave = tid >> 6;
-    for (int base = 0; base < T; base += kThreads * kScanItems) {
+    for (int base = 0; base < T; base += NT * kScanItems) {
       uint64_t x[kScanItems];
       const int i0 = base + tid * kScanItems;
 #pragma unroll
@@ -214,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
       __syncthreads();
       uint64_t wave_off = 0, tile_total = 0;
 #pragma unroll
-      for (int i = 0; i < kWaves; ++i) {
+      for (int i = 0; i < NT / 64; ++i) {
         wave_off += i < wave ? sh.red_u64[i] : 0;
         tile_total += sh.red_u64[i];
       }
@@ -231,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
 
   // -- step 3b: thresholds theta_k = min(V, ceil(k*Delta*V)), cuts e_k
   int32_t* en = ends + size_t(n) * (P.n_thr + 1);
-  for (int kk = tid; kk < P.n_thr; kk += kThreads) {
+  for (int kk = tid; kk < P.n_thr; kk += NT) {
     if (P.seg_fixed > 0) {  // ablation: a cut every seg_fixed positions
       const int64_t e = int64_t(kk + 1) * P.seg_fixed - 1;
       en[kk] = e < T - 1 ? int(e) : T - 1;  // cuts past the end collapse into T-1
@@ -297,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
   const size_t so = size_t(n) * P.s_cap;
   int64_t f_part = 0;
   uint64_t m_part = 0;
-  for (int s = tid; s < ns; s += kThreads) {
+  for (int s = tid; s < ns; s += NT) {
     int lo = 0, hi = nm - 1;  // merged segment holding piece s
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -331,16 +392,16 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
     f_part += fl;
     m_part += mass;
   }
-  const int64_t F = block_sum_i64(f_part, sh);
-  const uint64_t SM = block_sum_u64(m_part, sh);
+  const int64_t F = block_sum_i64<NT>(f_part, sh);
+  const uint64_t SM = block_sum_u64<NT>(m_part, sh);
 
   // -- step 3f/3g: quotas
   if (F > mk.t_keep) {
-    for (int s = tid; s < ns; s += kThreads) seg_q[so + s] = seg_f[so + s];
+    for (int s = tid; s < ns; s += NT) seg_q[so + s] = seg_f[so + s];
   } else {
     const int64_t t_rem = mk.t_keep - F;
     int64_t q_part = 0;
-    for (int s = tid; s < ns; s += kThreads) {
+    for (int s = tid; s < ns; s += NT) {
       int64_t add = 0;
       if (SM > 0) {
         const double share = double(t_rem) * (double(seg_m[so + s]) / double(SM));
@@ -351,49 +412,61 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
       seg_q[so + s] = int32_t(qv);
       q_part += qv;
     }
-    const int64_t D = int64_t(mk.t_keep) - block_sum_i64(q_part, sh);
+    const int64_t D = int64_t(mk.t_keep) - block_sum_i64<NT>(q_part, sh);
     if (D != 0) {
       // Cyclic walk in closed form: c full cycles give every segment
       // min(room, c); the next, partial cycle gives one more to the first r
       // segments (in walk order) whose room exceeds c.
       const bool adding = D > 0;
       const int64_t need = adding ? D : -D;
+      // Rooms and walk keys go to LDS when they fit (the ranks below read
+      // every segment once per segment).
+      const bool staged = ns <= Shared<NT>::kRankStage;
+      if (staged) {
+        for (int s = tid; s < ns; s += NT) {
+          sh.u.walk.room[s] = adding ? seg_a[so + s] - seg_q[so + s] : seg_q[so + s] - seg_f[so + s];
+          sh.u.walk.m[s] = seg_m[so + s];
+        }
+        __syncthreads();
+      }
+      auto room_of = [&](int s) -> int64_t {
+        if (staged) return sh.u.walk.room[s];
+        return adding ? seg_a[so + s] - seg_q[so + s] : seg_q[so + s] - seg_f[so + s];
+      };
+      auto m_of = [&](int s) -> uint64_t { return staged ? sh.u.walk.m[s] : seg_m[so + s]; };
       int64_t rmax = 0;
-      for (int s = tid; s < ns; s += kThreads) {
-        const int64_t room = adding ? seg_a[so + s] - seg_q[so + s] : seg_q[so + s] - seg_f[so + s];
+      for (int s = tid; s < ns; s += NT) {
+        const int64_t room = room_of(s);
         rmax = room > rmax ? room : rmax;
       }
-      rmax = block_max_i64(rmax, sh);
+      rmax = block_max_i64<NT>(rmax, sh);
       int64_t lo = 0, hi = rmax;
       while (lo < hi) {  // largest c with sum min(room, c) <= need
         const int64_t mid = (lo + hi + 1) >> 1;
         int64_t sp = 0;
-        for (int s = tid; s < ns; s += kThreads) {
-          const int64_t room =
-              adding ? seg_a[so + s] - seg_q[so + s] : seg_q[so + s] - seg_f[so + s];
+        for (int s = tid; s < ns; s += NT) {
+          const int64_t room = room_of(s);
           sp += room < mid ? room : mid;
         }
-        if (block_sum_i64(sp, sh) <= need) lo = mid; else hi = mid - 1;
+        if (block_sum_i64<NT>(sp, sh) <= need) lo = mid; else hi = mid - 1;
       }
       const int64_t cyc = lo;
       int64_t sp = 0;
-      for (int s = tid; s < ns; s += kThreads) {
-        const int64_t room = adding ? seg_a[so + s] - seg_q[so + s] : seg_q[so + s] - seg_f[so + s];
+      for (int s = tid; s < ns; s += NT) {
+        const int64_t room = room_of(s);
         sp += room < cyc ? room : cyc;
       }
-      const int64_t r = need - block_sum_i64(sp, sh);
-      // New quotas go to the output array; the ranks read the old rooms in
-      // seg_q, which nothing writes during this loop.
-      for (int s = tid; s < ns; s += kThreads) {
-        const int64_t room = adding ? seg_a[so + s] - seg_q[so + s] : seg_q[so + s] - seg_f[so + s];
+      const int64_t r = need - block_sum_i64<NT>(sp, sh);
+      // New quotas go to the output array; the ranks read the old rooms,
+      // which nothing writes during this loop.
+      for (int s = tid; s < ns; s += NT) {
+        const int64_t room = room_of(s);
         int64_t delta = room < cyc ? room : cyc;
         if (room > cyc && r > 0) {
-          const uint64_t ms = seg_m[so + s];
+          const uint64_t ms = m_of(s);
           int64_t rank = 0;
-          for (int o = 0; o < ns && rank < r; ++o) {
-            const int64_t ro = adding ? seg_a[so + o] - seg_q[so + o] : seg_q[so + o] - seg_f[so + o];
-            if (ro > cyc && precedes(seg_m[so + o], o, ms, s, adding)) ++rank;
-          }
+          for (int o = 0; o < ns && rank < r; ++o)
+            if (room_of(o) > cyc && precedes(m_of(o), o, ms, s, adding)) ++rank;
           if (rank < r) ++delta;
         }
         seg_quota[so + s] = int32_t(adding ? seg_q[so + s] + delta : seg_q[so + s] - delta);
@@ -403,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void k_mass_segment(
     }
   }
   __syncthreads();
-  for (int s = tid; s < ns; s += kThreads) seg_quota[so + s] = seg_q[so + s];
+  for (int s = tid; s < ns; s += NT) seg_quota[so + s] = seg_q[so + s];
   if (tid == 0) n_seg[n] = ns;
 }
 
@@ -414,8 +487,12 @@ hipError_t launch_mass_segment(const Derived& d, const float* u, const uint64_t*
                                int32_t* seg_start, int32_t* seg_quota, int32_t* n_seg,
                                uint64_t* seg_m, int32_t* seg_a, int32_t* seg_f, int32_t* seg_q,
                                int32_t* ends, hipStream_t s) {
-  k_mass_segment<<<d.NH, kThreads, 0, s>>>(d, u, credit_in, score, credit_upd, vp, seg_start,
-                                          seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q, ends);
+  if (d.T >= 4096)
+    k_mass_segment<1024><<<d.NH, 1024, 0, s>>>(d, u, credit_in, score, credit_upd, vp, seg_start,
+                                              seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q, ends);
+  else
+    k_mass_segment<256><<<d.NH, 256, 0, s>>>(d, u, credit_in, score, credit_upd, vp, seg_start,
+                                            seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q, ends);
   return hipGetLastError();
 }
 

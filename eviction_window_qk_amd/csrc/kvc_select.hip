@@ -18,14 +18,15 @@
 namespace kvc {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+// Long caches run with 1024 threads per workgroup, short ones with 256.
+constexpr int kMaxWaves = 16;
+constexpr int kCached = 16;    // keys per thread kept in registers by the threshold search
 constexpr int kWaveSeg = 256;  // segments up to this length: one wave each
 constexpr int kPerLane = kWaveSeg / 64;
 
 struct Shared {
   uint32_t bits[kMaxT / 32];
-  uint32_t red[kWaves];
+  uint32_t red[kMaxWaves];
 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -47,6 +48,7 @@ __device__ __forceinline__ void clear_bit(Shared& sh, int t) {
 }
 
 // Block-wide count; every thread must call it.
+template <int NT>
 __device__ uint32_t block_count(uint32_t c, Shared& sh) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
@@ -55,35 +57,72 @@ __device__ uint32_t block_count(uint32_t c, Shared& sh) {
   __syncthreads();
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) s += sh.red[i];
+  for (int i = 0; i < NT / 64; ++i) s += sh.red[i];
   return s;
 }
 
 // The r best positions of {t in [a,b] : pred(t)} are those with key > tau,
 // plus those with key == tau and t <= xcut.  Requires 1 <= r < |set|; every
-// thread must call it with the same arguments.
-template <class Pred>
+// thread must call it with the same arguments.  tau is found bit by bit (the
+// largest key with at least r members >= it), xcut by a binary search over
+// positions.  When the range fits, each thread first caches its candidates'
+// keys in registers (kCached per thread), so the 32 + log2(L) counting rounds
+// read no memory; otherwise they re-read the scores.
+template <int NT, class Pred>
 __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint32_t r, Pred pred,
                                 Shared& sh, uint32_t* tau_out, int* xcut_out) {
   uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    uint32_t c = 0;
-    for (int t = a + threadIdx.x; t <= b; t += kThreads)
-      c += (pred(t) && order_key(sc[t]) >= cand) ? 1u : 0u;
-    if (block_count(c, sh) >= r) tau = cand;
-  }
-  uint32_t c = 0;
-  for (int t = a + threadIdx.x; t <= b; t += kThreads)
-    c += (pred(t) && order_key(sc[t]) > tau) ? 1u : 0u;
-  const uint32_t need = r - block_count(c, sh);
   int lo = a, hi = b;
-  while (lo < hi) {
-    const int mid = lo + ((hi - lo) >> 1);
-    uint32_t e = 0;
-    for (int t = a + threadIdx.x; t <= mid; t += kThreads)
-      e += (pred(t) && order_key(sc[t]) == tau) ? 1u : 0u;
-    if (block_count(e, sh) >= need) hi = mid; else lo = mid + 1;
+  if (b - a + 1 <= NT * kCached) {
+    uint32_t key[kCached];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int i = 0; i < kCached; ++i) {
+      const int t = a + int(threadIdx.x) + i * NT;
+      const bool ok = t <= b && pred(t);
+      key[i] = ok ? order_key(sc[t]) : 0u;
+      valid |= ok ? (1u << i) : 0u;
+    }
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < kCached; ++i) c += ((valid >> i) & 1u) && key[i] >= cand ? 1u : 0u;
+      if (block_count<NT>(c, sh) >= r) tau = cand;
+    }
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < kCached; ++i) c += ((valid >> i) & 1u) && key[i] > tau ? 1u : 0u;
+    const uint32_t need = r - block_count<NT>(c, sh);
+    while (lo < hi) {
+      const int mid = lo + ((hi - lo) >> 1);
+      uint32_t e = 0;
+#pragma unroll
+      for (int i = 0; i < kCached; ++i) {
+        const int t = a + int(threadIdx.x) + i * NT;
+        e += ((valid >> i) & 1u) && t <= mid && key[i] == tau ? 1u : 0u;
+      }
+      if (block_count<NT>(e, sh) >= need) hi = mid; else lo = mid + 1;
+    }
+  } else {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      uint32_t c = 0;
+      for (int t = a + threadIdx.x; t <= b; t += NT)
+        c += (pred(t) && order_key(sc[t]) >= cand) ? 1u : 0u;
+      if (block_count<NT>(c, sh) >= r) tau = cand;
+    }
+    uint32_t c = 0;
+    for (int t = a + threadIdx.x; t <= b; t += NT)
+      c += (pred(t) && order_key(sc[t]) > tau) ? 1u : 0u;
+    const uint32_t need = r - block_count<NT>(c, sh);
+    while (lo < hi) {
+      const int mid = lo + ((hi - lo) >> 1);
+      uint32_t e = 0;
+      for (int t = a + threadIdx.x; t <= mid; t += NT)
+        e += (pred(t) && order_key(sc[t]) == tau) ? 1u : 0u;
+      if (block_count<NT>(e, sh) >= need) hi = mid; else lo = mid + 1;
+    }
   }
   *tau_out = tau;
   *xcut_out = lo;
@@ -91,7 +130,8 @@ __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint
 
 __device__ __forceinline__ uint32_t wave_count(bool v) { return __popcll(__ballot(v)); }
 
-__global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __restrict__ score,
+template <int NT>
+__global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restrict__ score,
                                                      const int32_t* __restrict__ seg_start,
                                                      const int32_t* __restrict__ seg_quota,
                                                      const int32_t* __restrict__ n_seg,
@@ -105,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* kn = kept + size_t(n) * K;
   if (T <= K) {  // nothing to evict: identity, -1 past T
-    for (int j = tid; j < K; j += kThreads) kn[j] = j < T ? sp.off + j : -1;
+    for (int j = tid; j < K; j += NT) kn[j] = j < T ? sp.off + j : -1;
     return;
   }
   const float* sc = score + size_t(n) * P.T + sp.off;
@@ -114,10 +154,10 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
   const int s_keep = mk.s, r_beg = T - mk.r;
   auto must_keep = [&](int t) { return t < s_keep || t >= r_beg; };
 
-  for (int w = tid; w < nw; w += kThreads) sh.bits[w] = 0;
+  for (int w = tid; w < nw; w += NT) sh.bits[w] = 0;
   __syncthreads();
-  for (int t = tid; t < s_keep; t += kThreads) set_bit(sh, t);
-  for (int t = r_beg + tid; t < T; t += kThreads) set_bit(sh, t);
+  for (int t = tid; t < s_keep; t += NT) set_bit(sh, t);
+  for (int t = r_beg + tid; t < T; t += NT) set_bit(sh, t);
 
   // Segments as given (sanitised to [0,T); empty ones are skipped).
   int ns = n_seg[n];
@@ -139,18 +179,18 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
     if (b - a + 1 <= kWaveSeg) continue;
     const int q = sq[i] < 0 ? 0 : sq[i];
     uint32_t c = 0;
-    for (int t = a + tid; t <= b; t += kThreads) c += must_keep(t) ? 0u : 1u;
-    const uint32_t avail = block_count(c, sh);
+    for (int t = a + tid; t <= b; t += NT) c += must_keep(t) ? 0u : 1u;
+    const uint32_t avail = block_count<NT>(c, sh);
     if (q == 0 || avail == 0) continue;
     if (uint32_t(q) >= avail) {
-      for (int t = a + tid; t <= b; t += kThreads)
+      for (int t = a + tid; t <= b; t += NT)
         if (!must_keep(t)) set_bit(sh, t);
       continue;
     }
     uint32_t tau;
     int xcut;
-    block_threshold(sc, a, b, uint32_t(q), [&](int t) { return !must_keep(t); }, sh, &tau, &xcut);
-    for (int t = a + tid; t <= b; t += kThreads) {
+    block_threshold<NT>(sc, a, b, uint32_t(q), [&](int t) { return !must_keep(t); }, sh, &tau, &xcut);
+    for (int t = a + tid; t <= b; t += NT) {
       if (must_keep(t)) continue;
       const uint32_t kk = order_key(sc[t]);
       if (kk > tau || (kk == tau && t <= xcut)) set_bit(sh, t);
@@ -158,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
   }
 
   // Short segments: one wave each, keys held in registers.
-  for (int i = wave; i < ns; i += kWaves) {
+  for (int i = wave; i < ns; i += (NT / 64)) {
     int a, b;
     seg_bounds(i, &a, &b);
     const int L = b - a + 1;
@@ -210,8 +250,8 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
 
   // Budget repair.
   uint32_t c = 0;
-  for (int w = tid; w < nw; w += kThreads) c += __popc(sh.bits[w]);
-  const uint32_t n_keep = block_count(c, sh);
+  for (int w = tid; w < nw; w += NT) c += __popc(sh.bits[w]);
+  const uint32_t n_keep = block_count<NT>(c, sh);
   const uint32_t n_mk = uint32_t(mk.s + mk.r);
   if (n_keep > uint32_t(K)) {
     // Keep the best K - |MK| picks, drop the rest (the lowest-scored first).
@@ -219,15 +259,15 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
     const uint32_t r = uint32_t(K) - n_mk;
     if (r == 0) {
       __syncthreads();
-      for (int t = tid; t < T; t += kThreads)
+      for (int t = tid; t < T; t += NT)
         if (!must_keep(t)) clear_bit(sh, t);
     } else {
       uint32_t tau;
       int xcut;
-      block_threshold(sc, 0, T - 1, r, is_pick, sh, &tau, &xcut);
+      block_threshold<NT>(sc, 0, T - 1, r, is_pick, sh, &tau, &xcut);
       // Each thread tests and clears only its own positions' bits.
       __syncthreads();
-      for (int t = tid; t < T; t += kThreads) {
+      for (int t = tid; t < T; t += NT) {
         if (must_keep(t) || !test_bit(sh, t)) continue;
         const uint32_t kk = order_key(sc[t]);
         if (!(kk > tau || (kk == tau && t <= xcut))) clear_bit(sh, t);
@@ -238,19 +278,19 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
     auto is_free = [&](int t) { return !must_keep(t) && !test_bit(sh, t); };
     const uint32_t r = uint32_t(K) - n_keep;
     uint32_t f = 0;
-    for (int t = tid; t < T; t += kThreads) f += is_free(t) ? 1u : 0u;
-    const uint32_t n_free = block_count(f, sh);
+    for (int t = tid; t < T; t += NT) f += is_free(t) ? 1u : 0u;
+    const uint32_t n_free = block_count<NT>(f, sh);
     if (r >= n_free) {
       __syncthreads();
-      for (int t = tid; t < T; t += kThreads)
+      for (int t = tid; t < T; t += NT)
         if (!must_keep(t)) set_bit(sh, t);
     } else {
       uint32_t tau;
       int xcut;
-      block_threshold(sc, 0, T - 1, r, is_free, sh, &tau, &xcut);
+      block_threshold<NT>(sc, 0, T - 1, r, is_free, sh, &tau, &xcut);
       // Each thread tests and sets only its own positions' bits.
       __syncthreads();
-      for (int t = tid; t < T; t += kThreads) {
+      for (int t = tid; t < T; t += NT) {
         if (!is_free(t)) continue;
         const uint32_t kk = order_key(sc[t]);
         if (kk > tau || (kk == tau && t <= xcut)) set_bit(sh, t);
@@ -260,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
   __syncthreads();
 
   // Compaction: ascending positions of the set bits.
-  const int wpt = (nw + kThreads - 1) / kThreads;
+  const int wpt = (nw + NT - 1) / NT;
   const int w0 = tid * wpt;
   uint32_t cnt = 0;
   for (int w = w0; w < w0 + wpt && w < nw; ++w) cnt += __popc(sh.bits[w]);
@@ -291,7 +331,10 @@ __global__ __launch_bounds__(kThreads) void k_select(Derived P, const float* __r
 hipError_t launch_select(const Derived& d, const float* score, const int32_t* seg_start,
                          const int32_t* seg_quota, const int32_t* n_seg, int32_t* kept,
                          hipStream_t s) {
-  k_select<<<d.NH, kThreads, 0, s>>>(d, score, seg_start, seg_quota, n_seg, kept);
+  if (d.T >= 4096)
+    k_select<1024><<<d.NH, 1024, 0, s>>>(d, score, seg_start, seg_quota, n_seg, kept);
+  else
+    k_select<256><<<d.NH, 256, 0, s>>>(d, score, seg_start, seg_quota, n_seg, kept);
   return hipGetLastError();
 }
 
