@@ -73,6 +73,11 @@ SMALL = [
     ("fine_delta", 2, 2, 16, 64, 900, 300, dict(delta=0.01, seg_min=2, seg_max=64), 1.0),
     ("q_min_3", 2, 2, 16, 64, 700, 150, dict(q_min=3, pool_kernel=3), 1.0),
     ("long_segments", 1, 2, 16, 64, 5000, 700, dict(seg_max=0, delta=0.3, seg_min=600), 1.0),
+    # a 1024-token cache (whole 64-key tiles), 120 query rows (not a multiple of the 256-row
+    # pass-1 workgroup), and a cache one position past a 256-key pass-2 chunk boundary
+    ("t1024_whole_tiles", 2, 2, 64, 128, 1024, 300, {}, 2.0),
+    ("rows_120", 2, 3, 40, 128, 777, 200, {}, 1.0),
+    ("t1025_chunk_edge", 2, 3, 40, 128, 1025, 200, {}, 1.0),
 ]
 
 
