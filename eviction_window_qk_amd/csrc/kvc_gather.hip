@@ -8,8 +8,14 @@
 // Pure data movement, bound by HBM bandwidth.  Each 16-byte piece of an
 // output row is one thread's dwordx4 load and store; consecutive threads
 // cover consecutive pieces, so a wave moves 4 (d = 128) or 8 (d = 64) whole
-// rows per instruction with fully coalesced accesses.  Each thread handles
-// kUnroll pieces spaced a grid apart, issuing all loads before the stores.
+// rows per instruction with fully coalesced accesses.  A workgroup copies a
+// run of one head's output rows (the head comes from the block index, no
+// per-element division), each thread kUnroll pieces a workgroup apart, all
+// loads issued before the stores.  Loads and stores are non-temporal: the
+// rows are touched once.  Against a grid-stride loop with cached accesses
+// this measured about 11 % faster on the long and large-budget events and
+// the same on the Qwen-7B event.  The credit of each output row moves in the
+// same workgroup.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -18,42 +24,54 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 2;       // pieces per thread, contiguous gather
+constexpr int kPagedUnroll = 4;  // pieces per thread, paged gather
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_gather(Derived P, const int32_t* __restrict__ kept,
                                                      const u32x4* __restrict__ k,
                                                      const u32x4* __restrict__ v,
+                                                     const uint64_t* __restrict__ cu,
                                                      u32x4* __restrict__ k_out,
-                                                     u32x4* __restrict__ v_out, size_t total) {
+                                                     u32x4* __restrict__ v_out,
+                                                     uint64_t* __restrict__ co, int h0) {
   constexpr int kPieces = D / 8;  // 16-byte pieces per row
-  const size_t stride = size_t(gridDim.x) * kThreads;
-  for (size_t base = size_t(blockIdx.x) * kThreads + threadIdx.x; base < total;
-       base += stride * kUnroll) {
-    u32x4 kv[kUnroll], vv[kUnroll];
+  constexpr int kRows = kThreads * kUnroll / kPieces;
+  const int chunks = (P.K + kRows - 1) / kRows;
+  const int n = h0 + int(blockIdx.x / chunks), r0 = int(blockIdx.x % chunks) * kRows;
+  const int32_t* kn = kept + size_t(n) * P.K;
+  const u32x4* kb = k + size_t(n) * P.TS * kPieces;
+  const u32x4* vb = v + size_t(n) * P.TS * kPieces;
+  u32x4 kv[kUnroll], vv[kUnroll];
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
-      const size_t idx = base + i * stride;
-      kv[i] = vv[i] = u32x4{0, 0, 0, 0};
-      if (idx < total) {
-        const size_t row = idx / kPieces;  // n * K + j
-        const int piece = int(idx % kPieces);
-        const size_t n = row / P.K;
-        const int t = kept[row];
-        if (t >= 0 && t < P.T) {
-          const size_t src = (n * P.TS + size_t(t)) * kPieces + piece;
-          kv[i] = k[src];
-          vv[i] = v[src];
-        }
+  for (int i = 0; i < kUnroll; ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    const int r = r0 + e / kPieces, piece = e % kPieces;
+    kv[i] = vv[i] = u32x4{0, 0, 0, 0};
+    if (r < P.K) {
+      const int t = kn[r];
+      if (t >= 0 && t < P.T) {
+        kv[i] = __builtin_nontemporal_load(&kb[size_t(t) * kPieces + piece]);
+        vv[i] = __builtin_nontemporal_load(&vb[size_t(t) * kPieces + piece]);
       }
     }
+  }
+  u32x4* kob = k_out + size_t(n) * P.K * kPieces;
+  u32x4* vob = v_out + size_t(n) * P.K * kPieces;
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
-      const size_t idx = base + i * stride;
-      if (idx < total) {
-        k_out[idx] = kv[i];
-        v_out[idx] = vv[i];
-      }
+  for (int i = 0; i < kUnroll; ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    const int r = r0 + e / kPieces, piece = e % kPieces;
+    if (r < P.K) {
+      __builtin_nontemporal_store(kv[i], &kob[size_t(r) * kPieces + piece]);
+      __builtin_nontemporal_store(vv[i], &vob[size_t(r) * kPieces + piece]);
+    }
+  }
+  if (co && threadIdx.x < kRows) {
+    const int r = r0 + threadIdx.x;
+    if (r < P.K) {
+      const int t = kn[r];
+      co[size_t(n) * P.K + r] = (t >= 0 && t < P.T) ? cu[size_t(n) * P.T + t] : 0;
     }
   }
 }
@@ -76,9 +94,10 @@ __global__ __launch_bounds__(kThreads) void k_gather_credit(Derived P,
 // copied from the kept original positions (through the old block table) into
 // consecutive slots of the new blocks.  Pools are [n_blocks][H][bs][D]; head n
 // = b * H + h.  Block ids outside [0, n_blocks) are never dereferenced: a bad
-// destination is skipped, a bad source gives a zero row.  Same thread mapping
-// as k_gather: kUnroll pieces a grid apart, so a thread's loads come from
-// unrelated rows and many table lookups are in flight at once.
+// destination is skipped, a bad source gives a zero row.  A grid-stride
+// loop, kPagedUnroll pieces a grid apart, so a thread's loads come from
+// unrelated rows and many table lookups are in flight at once (per-head
+// workgroups measured slower here); non-temporal like k_gather.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_gather_paged(
     Derived P, const int32_t* __restrict__ kept, const u32x4* __restrict__ k,
@@ -88,11 +107,11 @@ __global__ __launch_bounds__(kThreads) void k_gather_paged(
   constexpr int kPieces = D / 8;
   const size_t stride = size_t(gridDim.x) * kThreads;
   for (size_t base = size_t(blockIdx.x) * kThreads + threadIdx.x; base < total;
-       base += stride * kUnroll) {
-    u32x4 kv[kUnroll], vv[kUnroll];
-    int64_t dst[kUnroll];
+       base += stride * kPagedUnroll) {
+    u32x4 kv[kPagedUnroll], vv[kPagedUnroll];
+    int64_t dst[kPagedUnroll];
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < kPagedUnroll; ++i) {
       const size_t idx = base + i * stride;
       kv[i] = vv[i] = u32x4{0, 0, 0, 0};
       dst[i] = -1;
@@ -109,17 +128,17 @@ __global__ __launch_bounds__(kThreads) void k_gather_paged(
           const int64_t sb = tin[size_t(b) * tin_blocks + t / bs];
           if (sb >= 0 && sb < n_blocks) {
             const int64_t src = ((sb * H + h) * bs + t % bs) * kPieces + piece;
-            kv[i] = k[src];
-            vv[i] = v[src];
+            kv[i] = __builtin_nontemporal_load(&k[src]);
+            vv[i] = __builtin_nontemporal_load(&v[src]);
           }
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < kPagedUnroll; ++i) {
       if (dst[i] >= 0) {
-        k_out[dst[i]] = kv[i];
-        v_out[dst[i]] = vv[i];
+        __builtin_nontemporal_store(kv[i], &k_out[dst[i]]);
+        __builtin_nontemporal_store(vv[i], &v_out[dst[i]]);
       }
     }
   }
@@ -135,7 +154,7 @@ hipError_t launch_gather_paged(const Derived& d, const int32_t* kept, const void
                                uint64_t* credit_out, hipStream_t s) {
   const size_t rows = size_t(d.NH) * d.K;
   const size_t total = rows * size_t(d.D / 8);
-  size_t blocks = (total + size_t(kThreads) * kUnroll - 1) / (size_t(kThreads) * kUnroll);
+  size_t blocks = (total + size_t(kThreads) * kPagedUnroll - 1) / (size_t(kThreads) * kPagedUnroll);
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
   const u32x4* kk = static_cast<const u32x4*>(k_pool);
@@ -161,23 +180,23 @@ hipError_t launch_gather_paged(const Derived& d, const int32_t* kept, const void
 hipError_t launch_gather(const Derived& d, const int32_t* kept, const void* k, const void* v,
                          const uint64_t* credit_upd, void* k_out, void* v_out,
                          uint64_t* credit_out, hipStream_t s) {
-  const size_t rows = size_t(d.NH) * d.K;
-  const size_t total = rows * size_t(d.D / 8);
-  size_t blocks = (total + size_t(kThreads) * kUnroll - 1) / (size_t(kThreads) * kUnroll);
-  if (blocks > 65536) blocks = 65536;
-  if (blocks < 1) blocks = 1;
+  // One run of kRows output rows of one head per workgroup; heads go in
+  // launches of at most 2^22 workgroups (the grid counts work-items in 32 bits).
+  const int rows = kThreads * kUnroll / (d.D / 8);
+  const int chunks = (d.K + rows - 1) / rows;
+  const int per_launch = (1 << 22) / chunks > 0 ? (1 << 22) / chunks : 1;
   const u32x4* kk = static_cast<const u32x4*>(k);
   const u32x4* vv = static_cast<const u32x4*>(v);
   u32x4* ko = static_cast<u32x4*>(k_out);
   u32x4* vo = static_cast<u32x4*>(v_out);
-  if (d.D == 128)
-    k_gather<128><<<unsigned(blocks), kThreads, 0, s>>>(d, kept, kk, vv, ko, vo, total);
-  else
-    k_gather<64><<<unsigned(blocks), kThreads, 0, s>>>(d, kept, kk, vv, ko, vo, total);
-  if (credit_upd && credit_out) {
-    size_t cb = (rows + kThreads - 1) / kThreads;
-    if (cb > 65536) cb = 65536;
-    k_gather_credit<<<unsigned(cb), kThreads, 0, s>>>(d, kept, credit_upd, credit_out);
+  uint64_t* co = credit_upd ? credit_out : nullptr;
+  for (int h0 = 0; h0 < d.NH; h0 += per_launch) {
+    const int nh = d.NH - h0 < per_launch ? d.NH - h0 : per_launch;
+    const unsigned blocks = unsigned(nh) * unsigned(chunks);
+    if (d.D == 128)
+      k_gather<128><<<blocks, kThreads, 0, s>>>(d, kept, kk, vv, credit_upd, ko, vo, co, h0);
+    else
+      k_gather<64><<<blocks, kThreads, 0, s>>>(d, kept, kk, vv, credit_upd, ko, vo, co, h0);
   }
   return hipGetLastError();
 }
