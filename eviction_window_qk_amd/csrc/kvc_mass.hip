@@ -29,9 +29,18 @@ namespace {
 // Long caches run with 1024 threads per workgroup (one head per CU is then
 // enough to keep the loads in flight); short ones with 256.
 constexpr int kMaxWaves = 16;
-constexpr int kScanItems = 4;
-constexpr int kSweep = 4;          // positions per thread per pooling tile
 constexpr int kMaxHalo = 31;       // pool_kernel <= 63
+
+// Positions per thread per pass iteration.  The long-cache variant runs one
+// workgroup per CU, so each thread keeps 8 loads per array in flight per
+// sweep; the short-cache one keeps its LDS small for several workgroups per
+// CU.  The scan reads 4 consecutive positions per thread (more measured
+// slower: the per-lane runs no longer share cache lines).
+template <int NT>
+struct Tune {
+  static constexpr int kSweep = NT >= 1024 ? 8 : 4;  // pooling tile, EMA sweeps
+  static constexpr int kScanItems = 4;               // prefix scan
+};
 constexpr int kMaxMerged = kMaxThresholds + 1;
 
 // LDS of one workgroup of NT threads (sized by NT so that the short-cache
@@ -46,7 +55,7 @@ struct Shared {
   int piece_off[kMaxMerged + 1];
   int n_merged;
   union {
-    float tile[NT * kSweep + 2 * kMaxHalo];  // pooling input tile with halo
+    float tile[NT * Tune<NT>::kSweep + 2 * kMaxHalo];  // pooling input tile with halo
     struct {
       uint64_t m[kRankStage];                // walk order keys (mass)
       int32_t room[kRankStage];              // steps left per segment
@@ -157,6 +166,8 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     uint64_t* __restrict__ seg_m, int32_t* __restrict__ seg_a, int32_t* __restrict__ seg_f,
     int32_t* __restrict__ seg_q, int32_t* __restrict__ ends) {
   __shared__ Shared<NT> sh;
+  constexpr int kSweep = Tune<NT>::kSweep;
+  constexpr int kScanItems = Tune<NT>::kScanItems;
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   // A left-padded head runs on its real tokens [off, off + T) only.
@@ -176,12 +187,20 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   uint64_t part = 0;
   const int h = P.pool_h;
   for (int t_base = 0; t_base < T; t_base += NT * kSweep) {
-    const int span = NT * kSweep + 2 * h;
-    __syncthreads();  // previous tile consumed
-    for (int i = tid; i < span; i += NT) {
-      const int t = t_base - h + i;
-      if (t >= 0 && t < T) sh.u.tile[i] = un[t];
+    const int span = NT * kSweep + 2 * h;  // <= NT * (kSweep + 1): 2h <= 62 < NT
+    // Every load of the tile is issued before any is stored: clamped indices
+    // instead of branches (slots outside [0, T) hold a copy never read).
+    float tv[kSweep + 1];
+#pragma unroll
+    for (int k = 0; k <= kSweep; ++k) {
+      int t = t_base - h + tid + k * NT;
+      t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+      tv[k] = un[t];
     }
+    __syncthreads();  // previous tile consumed
+#pragma unroll
+    for (int k = 0; k <= kSweep; ++k)
+      if (tid + k * NT < span) sh.u.tile[tid + k * NT] = tv[k];
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kSweep; ++k) {
@@ -207,10 +226,17 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
       uint64_t w[kSweep], cin[kSweep];
 #pragma unroll
-      for (int k = 0; k < kSweep; ++k) {  // loads first
+      for (int k = 0; k < kSweep; ++k) {  // loads first, clamped (no branches)
         const int t = t0 + k * NT;
-        w[k] = t < T ? vn[t] : 0;
-        cin[k] = t < T && t < P.n_prev ? ci[t] : 0;
+        w[k] = vn[t < T ? t : T - 1];
+        cin[k] = 0;
+      }
+      if (P.n_prev > 0) {
+#pragma unroll
+        for (int k = 0; k < kSweep; ++k) {
+          const int t = t0 + k * NT;
+          cin[k] = ci[t < P.n_prev ? t : P.n_prev - 1];
+        }
       }
 #pragma unroll
       for (int k = 0; k < kSweep; ++k) {
@@ -229,10 +255,10 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
       uint64_t w[kSweep], cq[kSweep];
 #pragma unroll
-      for (int k = 0; k < kSweep; ++k) {
+      for (int k = 0; k < kSweep; ++k) {  // clamped loads (positions past T are skipped below)
         const int t = t0 + k * NT;
-        w[k] = t < T ? vn[t] : 0;
-        cq[k] = t < T ? cu[t] : 0;
+        w[k] = vn[t < T ? t : T - 1];
+        cq[k] = cu[t < T ? t : T - 1];
       }
 #pragma unroll
       for (int k = 0; k < kSweep; ++k) {
@@ -261,7 +287,9 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
       uint64_t x[kScanItems];
       const int i0 = base + tid * kScanItems;
 #pragma unroll
-      for (int i = 0; i < kScanItems; ++i) x[i] = i0 + i < T ? vn[i0 + i] : 0;
+      for (int i = 0; i < kScanItems; ++i) x[i] = vn[i0 + i < T ? i0 + i : T - 1];
+#pragma unroll
+      for (int i = 0; i < kScanItems; ++i) x[i] = i0 + i < T ? x[i] : 0;
 #pragma unroll
       for (int i = 1; i < kScanItems; ++i) x[i] += x[i - 1];
       uint64_t incl = x[kScanItems - 1];
@@ -465,8 +493,19 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
         if (room > cyc && r > 0) {
           const uint64_t ms = m_of(s);
           int64_t rank = 0;
-          for (int o = 0; o < ns && rank < r; ++o)
-            if (room_of(o) > cyc && precedes(m_of(o), o, ms, s, adding)) ++rank;
+          if (staged) {  // every thread reads the same entry: LDS broadcasts, no branches
+            int o = 0;
+            for (; o + 4 <= ns; o += 4)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                rank += (sh.u.walk.room[o + i] > cyc) &
+                        precedes(sh.u.walk.m[o + i], o + i, ms, s, adding);
+            for (; o < ns; ++o)
+              rank += (sh.u.walk.room[o] > cyc) & precedes(sh.u.walk.m[o], o, ms, s, adding);
+          } else {
+            for (int o = 0; o < ns && rank < r; ++o)
+              if (room_of(o) > cyc && precedes(m_of(o), o, ms, s, adding)) ++rank;
+          }
           if (rank < r) ++delta;
         }
         seg_quota[so + s] = int32_t(adding ? seg_q[so + s] + delta : seg_q[so + s] - delta);
