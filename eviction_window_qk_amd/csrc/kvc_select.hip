@@ -77,10 +77,11 @@ __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint
     uint32_t key[kCached];
     uint32_t valid = 0;
 #pragma unroll
-    for (int i = 0; i < kCached; ++i) {
+    for (int i = 0; i < kCached; ++i) {  // clamped loads: all issued before any is used
       const int t = a + int(threadIdx.x) + i * NT;
+      const float x = sc[t <= b ? t : b];
       const bool ok = t <= b && pred(t);
-      key[i] = ok ? order_key(sc[t]) : 0u;
+      key[i] = ok ? order_key(x) : 0u;
       valid |= ok ? (1u << i) : 0u;
     }
     for (int bit = 31; bit >= 0; --bit) {
@@ -209,10 +210,11 @@ __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restric
     uint32_t key[kPerLane];
     uint32_t avail = 0;
 #pragma unroll
-    for (int e = 0; e < kPerLane; ++e) {
+    for (int e = 0; e < kPerLane; ++e) {  // clamped loads: all issued before any is used
       const int t = a + lane + 64 * e;
+      const float x = sc[t <= b ? t : b];
       ok[e] = t <= b && !must_keep(t);
-      key[e] = ok[e] ? order_key(sc[t]) : 0u;
+      key[e] = ok[e] ? order_key(x) : 0u;
       avail += wave_count(ok[e]);
     }
     if (uint32_t(q) >= avail) {
