@@ -24,9 +24,18 @@ constexpr int kCached = 16;    // keys per thread kept in registers by the thres
 constexpr int kWaveSeg = 256;  // segments up to this length: one wave each
 constexpr int kPerLane = kWaveSeg / 64;
 
+// LDS of one workgroup of NT threads: the keep bitmap (the short-cache
+// variant only takes caches below 4096 positions, so its bitmap is small and
+// several workgroups share a CU) and, for that variant, the segment starts
+// and quotas when they fit (every thread reads each of them once per loop).
+template <int NT>
 struct Shared {
-  uint32_t bits[kMaxT / 32];
+  static constexpr int kBits = NT >= 1024 ? kMaxT / 32 : 4096 / 32;
+  static constexpr int kStage = NT >= 1024 ? 1 : 512;
+  uint32_t bits[kBits];
   uint32_t red[kMaxWaves];
+  int32_t seg_s[kStage];
+  int32_t seg_q[kStage];
 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -35,21 +44,24 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ bool test_bit(const Shared& sh, int t) {
+template <class Sh>
+__device__ __forceinline__ bool test_bit(const Sh& sh, int t) {
   return (sh.bits[t >> 5] >> (t & 31)) & 1u;
 }
 
-__device__ __forceinline__ void set_bit(Shared& sh, int t) {
+template <class Sh>
+__device__ __forceinline__ void set_bit(Sh& sh, int t) {
   atomicOr(&sh.bits[t >> 5], 1u << (t & 31));
 }
 
-__device__ __forceinline__ void clear_bit(Shared& sh, int t) {
+template <class Sh>
+__device__ __forceinline__ void clear_bit(Sh& sh, int t) {
   atomicAnd(&sh.bits[t >> 5], ~(1u << (t & 31)));
 }
 
 // Block-wide count; every thread must call it.
 template <int NT>
-__device__ uint32_t block_count(uint32_t c, Shared& sh) {
+__device__ uint32_t block_count(uint32_t c, Shared<NT>& sh) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
   __syncthreads();
@@ -70,7 +82,7 @@ __device__ uint32_t block_count(uint32_t c, Shared& sh) {
 // read no memory; otherwise they re-read the scores.
 template <int NT, class Pred>
 __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint32_t r, Pred pred,
-                                Shared& sh, uint32_t* tau_out, int* xcut_out) {
+                                Shared<NT>& sh, uint32_t* tau_out, int* xcut_out) {
   uint32_t tau = 0;
   int lo = a, hi = b;
   if (b - a + 1 <= NT * kCached) {
@@ -137,7 +149,7 @@ __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restric
                                                      const int32_t* __restrict__ seg_quota,
                                                      const int32_t* __restrict__ n_seg,
                                                      int32_t* __restrict__ kept) {
-  __shared__ Shared sh;
+  __shared__ Shared<NT> sh;
   const int n = blockIdx.x;
   // A left-padded head runs on its real tokens [off, off + T) only; kept
   // holds positions of the padded cache.
@@ -155,18 +167,28 @@ __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restric
   const int s_keep = mk.s, r_beg = T - mk.r;
   auto must_keep = [&](int t) { return t < s_keep || t >= r_beg; };
 
-  for (int w = tid; w < nw; w += NT) sh.bits[w] = 0;
-  __syncthreads();
-  for (int t = tid; t < s_keep; t += NT) set_bit(sh, t);
-  for (int t = r_beg + tid; t < T; t += NT) set_bit(sh, t);
-
   // Segments as given (sanitised to [0,T); empty ones are skipped).
   int ns = n_seg[n];
   ns = ns < 0 ? 0 : (ns > P.s_cap ? P.s_cap : ns);
   const int32_t* ss = seg_start + size_t(n) * P.s_cap;
   const int32_t* sq = seg_quota + size_t(n) * P.s_cap;
+  const bool staged = NT < 1024 && ns <= Shared<NT>::kStage;
+  for (int w = tid; w < nw; w += NT) sh.bits[w] = 0;
+  if (staged)
+    for (int i = tid; i < ns; i += NT) {
+      sh.seg_s[i] = ss[i];
+      sh.seg_q[i] = sq[i];
+    }
+  __syncthreads();
+  for (int t = tid; t < s_keep; t += NT) set_bit(sh, t);
+  for (int t = r_beg + tid; t < T; t += NT) set_bit(sh, t);
+  auto start_of = [&](int i) { return staged ? sh.seg_s[i] : ss[i]; };
+  auto quota_of = [&](int i) {
+    const int q = staged ? sh.seg_q[i] : sq[i];
+    return q < 0 ? 0 : q;
+  };
   auto seg_bounds = [&](int i, int* a, int* b) {  // starts are padded-cache positions
-    int s0 = ss[i] - sp.off, s1 = i + 1 < ns ? ss[i + 1] - sp.off : T;
+    int s0 = start_of(i) - sp.off, s1 = i + 1 < ns ? start_of(i + 1) - sp.off : T;
     s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
     s1 = s1 < 0 ? 0 : (s1 > T ? T : s1);
     *a = s0;
@@ -178,7 +200,7 @@ __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restric
     int a, b;
     seg_bounds(i, &a, &b);
     if (b - a + 1 <= kWaveSeg) continue;
-    const int q = sq[i] < 0 ? 0 : sq[i];
+    const int q = quota_of(i);
     uint32_t c = 0;
     for (int t = a + tid; t <= b; t += NT) c += must_keep(t) ? 0u : 1u;
     const uint32_t avail = block_count<NT>(c, sh);
@@ -204,7 +226,7 @@ __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restric
     seg_bounds(i, &a, &b);
     const int L = b - a + 1;
     if (L <= 0 || L > kWaveSeg) continue;
-    const int q = sq[i] < 0 ? 0 : sq[i];
+    const int q = quota_of(i);
     if (q == 0) continue;
     bool ok[kPerLane];
     uint32_t key[kPerLane];
