@@ -108,6 +108,17 @@ def test_ema_credit(n_prev):
               label=f"ema{n_prev}")
 
 
+def test_ema_credit_long_cache():
+    """EMA with carried credit on a cache long enough (>= 4096) for the
+    1024-thread mass/segment and select workgroups."""
+    NH, G, W, d, T, K, n_prev = 2, 2, 16, 64, 5000, 600, 600
+    q, k, v = synth.random_small(4242, NH, G, W, d, T, key_scale=2.0)
+    rng = np.random.default_rng(17)
+    credit = (rng.random((NH, n_prev)) * 2.0 ** 37).astype(np.uint64)
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K, ema=True, lam=0.9, beta=0.9)
+    _run_case(pd, q, k, v, credit_in=credit, n_prev=n_prev, label="ema_long")
+
+
 def test_qwen7b_shape_heads():
     wl = synth.WORKLOADS["qwen7b_t768"]
     heads = [0, 1, 777, 1791]
