@@ -34,7 +34,6 @@ SOURCES = {
     "kvc_mass.hip": ["-ffp-contract=off"],
     "kvc_select.hip": [],
     "kvc_gather.hip": [],
-    "kvc_event.hip": ["-ffp-contract=off"],  # includes the mass/segment device code
     "kvc_refresh.hip": ["-ffp-contract=off"],  # fp64 cosine: one operation at a time
 }
 EXPORTS = ["kvc_score_window", "kvc_mass_segment", "kvc_select", "kvc_gather_compact",

@@ -459,16 +459,6 @@ int kvc_compress_event(const kvc_params* p, const void* q_win, const void* k, co
 
   rc = launch_status(launch_score(d, q_win, k, u, reinterpret_cast<float*>(w + L.stats), s));
   if (rc != KVC_OK) return rc;
-  if (d.T < kFusedTailT) {  // steps 2-5 in one kernel, one workgroup per head-event
-    rc = launch_status(launch_event_tail(
-        d, u, credit_in, score, cupd, reinterpret_cast<uint64_t*>(w + L.vp), seg_start, seg_quota,
-        n_seg, reinterpret_cast<uint64_t*>(w + L.seg_m), reinterpret_cast<int32_t*>(w + L.seg_a),
-        reinterpret_cast<int32_t*>(w + L.seg_f), reinterpret_cast<int32_t*>(w + L.seg_q),
-        reinterpret_cast<int32_t*>(w + L.ends), kept_out, k, v, k_out, v_out,
-        d.ema ? credit_out : nullptr, s));
-    if (rc != KVC_OK) return rc;
-    return (d.T <= d.K && !d.vlen) ? KVC_NOOP : KVC_OK;
-  }
   rc = launch_status(launch_mass_segment(
       d, u, credit_in, score, cupd, reinterpret_cast<uint64_t*>(w + L.vp), seg_start, seg_quota,
       n_seg, reinterpret_cast<uint64_t*>(w + L.seg_m), reinterpret_cast<int32_t*>(w + L.seg_a),

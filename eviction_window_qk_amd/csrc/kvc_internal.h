@@ -86,15 +86,6 @@ hipError_t launch_gather_paged(const Derived& d, const int32_t* kept, const void
                                void* v_pool_out, const uint64_t* credit_upd,
                                uint64_t* credit_out, hipStream_t s);
 
-// Steps 2-5 in one kernel (caches below kFusedTailT positions).
-constexpr int kFusedTailT = 4096;
-hipError_t launch_event_tail(const Derived& d, const float* u, const uint64_t* credit_in,
-                             float* score, uint64_t* credit_upd, uint64_t* vp, int32_t* seg_start,
-                             int32_t* seg_quota, int32_t* n_seg, uint64_t* seg_m, int32_t* seg_a,
-                             int32_t* seg_f, int32_t* seg_q, int32_t* ends, int32_t* kept,
-                             const void* k, const void* v, void* k_out, void* v_out,
-                             uint64_t* credit_out, hipStream_t s);
-
 hipError_t launch_qc_trigger(int rows, int Hq, int d, const void* q, double* q_ref, double thr,
                              int update, int32_t* full, double* cos_out, hipStream_t s);
 hipError_t launch_partial_init(int NH, int K, int T, const int32_t* kept, const float* score,

@@ -1,9 +1,162 @@
-// Steps 2 and 3 on gfx950: the stage kernel, one workgroup per head-event.
-// The device code (and its sources) is in kvc_mass_dev.h.
-#include "kvc_mass_dev.h"
+// Steps 2 and 3 on gfx950: mass, EMA credit, prefix, cuts, split/merge,
+// must-keep and quotas.  One workgroup per head-event (1024 threads for long
+// caches, 256 otherwise).
+//
+// Sources: AMS notes, key design 1 (m_i = (max(u_i,0)+eps)/sum; c <-
+// lambda*c + (1-lambda)*m; m_used = normalize(beta*m + (1-beta)*normalize(c));
+// small-kernel 1-D average pooling), key design 2 (C(t) = sum_{u<=t} m_u,
+// b_k = min{t : C(t) >= k*Delta}, long segments split into near-equal pieces,
+// short neighbours merged, masses recounted), key design 3 (must-keep sinks
+// and recent suffix first, shorten the suffix when short of budget,
+// q_i^min = min(q_min, L_i), T_rem split by segment mass with rounding, clip
+// and redistribute).
+//
+// Every integer decision is bit-identical to a sequential evaluation:
+//  - reductions (totals, prefix, segment masses) are unsigned 64-bit
+//    fixed-point sums, exact in any order;
+//  - each floating-point expression is evaluated one IEEE operation at a time
+//    in the written order (contraction is off for this file; division is
+//    correctly rounded), non-negative values are truncated toward zero;
+//  - usage is held as trunc(ubar * 2^40) + ceil(eps * 2^40), credit and mixed
+//    mass as Q44.
+#pragma clang fp contract(off)
+
+#include "kvc_internal.h"
 
 namespace kvc {
 namespace {
+
+// Long caches run with 1024 threads per workgroup (one head per CU is then
+// enough to keep the loads in flight); short ones with 256.
+constexpr int kMaxWaves = 16;
+constexpr int kMaxHalo = 31;       // pool_kernel <= 63
+
+// Positions per thread per pass iteration.  The long-cache variant runs one
+// workgroup per CU, so each thread keeps 8 loads per array in flight per
+// sweep; the short-cache one keeps its LDS small for several workgroups per
+// CU.  The scan reads 4 consecutive positions per thread (more measured
+// slower: the per-lane runs no longer share cache lines).
+template <int NT>
+struct Tune {
+  static constexpr int kSweep = NT >= 1024 ? 8 : 4;  // pooling tile, EMA sweeps
+  static constexpr int kScanItems = 4;               // prefix scan
+};
+constexpr int kMaxMerged = kMaxThresholds + 1;
+
+// LDS of one workgroup of NT threads (sized by NT so that the short-cache
+// variant keeps several workgroups per CU).
+template <int NT>
+struct Shared {
+  static constexpr int kRankStage = 2 * NT;  // segments whose walk data fit LDS
+  uint64_t red_u64[kMaxWaves];
+  int64_t red_i64[kMaxWaves];
+  int merged_a[kMaxMerged];
+  int merged_b[kMaxMerged];
+  int piece_off[kMaxMerged + 1];
+  int n_merged;
+  union {
+    float tile[NT * Tune<NT>::kSweep + 2 * kMaxHalo];  // pooling input tile with halo
+    struct {
+      uint64_t m[kRankStage];                // walk order keys (mass)
+      int32_t room[kRankStage];              // steps left per segment
+    } walk;
+  } u;
+};
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ int64_t wave_max_i64(int64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const int64_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Block-wide reductions: every thread must call them (uniform control flow).
+template <int NT>
+__device__ uint64_t block_sum_u64(uint64_t v, Shared<NT>& sh) {
+  v = wave_sum_u64(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.red_u64[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t s = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += sh.red_u64[i];
+  return s;
+}
+
+template <int NT>
+__device__ int64_t block_sum_i64(int64_t v, Shared<NT>& sh) {
+  v = wave_sum_i64(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.red_i64[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int64_t s = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += sh.red_i64[i];
+  return s;
+}
+
+template <int NT>
+__device__ int64_t block_max_i64(int64_t v, Shared<NT>& sh) {
+  v = wave_max_i64(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.red_i64[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int64_t s = sh.red_i64[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) s = sh.red_i64[i] > s ? sh.red_i64[i] : s;
+  return s;
+}
+
+// Pooled usage at t: centred window of 2h+1, in-range neighbours only.
+// Average: fp32 sum in ascending position order from +0.0, one division.
+// `tile` holds positions [t_base - h, ...) of the head (only in-range
+// positions are ever read).
+__device__ __forceinline__ float pooled(const float* __restrict__ tile, int t_base, int T, int t,
+                                        int h, int mode) {
+  const int lo = t - h < 0 ? 0 : t - h;
+  const int hi = t + h > T - 1 ? T - 1 : t + h;
+  const float* x = tile + (h - t_base);  // x[j] = u[j]
+  if (mode == KVC_POOL_MAX) {
+    float m = x[lo];
+    for (int j = lo + 1; j <= hi; ++j) m = fmaxf(m, x[j]);
+    return m;
+  }
+  float acc = 0.0f;
+  for (int j = lo; j <= hi; ++j) acc = acc + x[j];
+  return acc / float(hi - lo + 1);
+}
+
+// Sum of v over [a, b] (inclusive, may be empty) from the inclusive prefix.
+__device__ __forceinline__ uint64_t range_sum(const uint64_t* __restrict__ P, int a, int b) {
+  if (a > b) return 0;
+  return P[b] - (a > 0 ? P[a - 1] : 0);
+}
+
+__device__ __forceinline__ int overlap_len(int a, int b, int c, int e) {
+  const int lo = a > c ? a : c, hi = b < e ? b : e;
+  return hi >= lo ? hi - lo + 1 : 0;
+}
+
+// Does segment x come before segment y in the redistribution order?
+// Adding: (mass desc, index asc); removing: (mass asc, index desc).
+__device__ __forceinline__ bool precedes(uint64_t mx, int x, uint64_t my, int y, bool adding) {
+  if (adding) return mx > my || (mx == my && x < y);
+  return mx < my || (mx == my && x > y);
+}
 
 template <int NT>
 __global__ __launch_bounds__(NT) void k_mass_segment(
@@ -12,9 +165,358 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     int32_t* __restrict__ seg_start, int32_t* __restrict__ seg_quota, int32_t* __restrict__ n_seg,
     uint64_t* __restrict__ seg_m, int32_t* __restrict__ seg_a, int32_t* __restrict__ seg_f,
     int32_t* __restrict__ seg_q, int32_t* __restrict__ ends) {
-  __shared__ mass::Shared<NT> sh;
-  mass::mass_segment_head<NT>(P, int(blockIdx.x), u, credit_in, score, credit_upd, vp, seg_start,
-                              seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q, ends, sh);
+  __shared__ Shared<NT> sh;
+  constexpr int kSweep = Tune<NT>::kSweep;
+  constexpr int kScanItems = Tune<NT>::kScanItems;
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  // A left-padded head runs on its real tokens [off, off + T) only.
+  const Span sp = head_span(P, n);
+  const int T = sp.T;
+  const Keep mk = P.vlen ? must_keep(P.sinks, P.recent, P.K, T) : Keep{P.s_keep, P.r_keep, P.t_keep};
+  const float* un = u + size_t(n) * P.T + sp.off;
+  float* sc = score + size_t(n) * P.T + sp.off;
+  uint64_t* vn = vp + size_t(n) * P.T + sp.off;
+  for (int t = tid; t < sp.off; t += NT) {  // padding: score 0, credit 0
+    score[size_t(n) * P.T + t] = 0.0f;
+    if (P.ema) credit_upd[size_t(n) * P.T + t] = 0;
+  }
+
+  // -- step 2a/2b: pooled score and fixed-point usage w = trunc(ubar*2^40)+e,
+  // one tile of NT*kSweep positions (plus the pooling halo) through LDS
+  uint64_t part = 0;
+  const int h = P.pool_h;
+  for (int t_base = 0; t_base < T; t_base += NT * kSweep) {
+    const int span = NT * kSweep + 2 * h;  // <= NT * (kSweep + 1): 2h <= 62 < NT
+    // Every load of the tile is issued before any is stored: clamped indices
+    // instead of branches (slots outside [0, T) hold a copy never read).
+    float tv[kSweep + 1];
+#pragma unroll
+    for (int k = 0; k <= kSweep; ++k) {
+      int t = t_base - h + tid + k * NT;
+      t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+      tv[k] = un[t];
+    }
+    __syncthreads();  // previous tile consumed
+#pragma unroll
+    for (int k = 0; k <= kSweep; ++k)
+      if (tid + k * NT < span) sh.u.tile[tid + k * NT] = tv[k];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSweep; ++k) {
+      const int t = t_base + k * NT + tid;
+      if (t < T) {
+        const float ub = pooled(sh.u.tile, t_base, T, t, h, P.pool_mode);
+        sc[t] = ub;
+        const float nonneg = ub > 0.0f ? ub : 0.0f;
+        const uint64_t w = uint64_t(nonneg * 1099511627776.0f) + P.eps_q;  // exact 2^40 scale
+        vn[t] = w;
+        part += w;
+      }
+    }
+  }
+  const uint64_t w_total = block_sum_u64<NT>(part, sh);
+
+  // -- step 2c: EMA credit and mixed mass (Q44)
+  if (P.ema) {
+    uint64_t* cu = credit_upd + size_t(n) * P.T + sp.off;
+    const uint64_t* ci = credit_in ? credit_in + size_t(n) * P.n_prev : nullptr;
+    const double wd = double(w_total);
+    part = 0;
+    for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
+      uint64_t w[kSweep], cin[kSweep];
+#pragma unroll
+      for (int k = 0; k < kSweep; ++k) {  // loads first, clamped (no branches)
+        const int t = t0 + k * NT;
+        w[k] = vn[t < T ? t : T - 1];
+        cin[k] = 0;
+      }
+      if (P.n_prev > 0) {
+#pragma unroll
+        for (int k = 0; k < kSweep; ++k) {
+          const int t = t0 + k * NT;
+          cin[k] = ci[t < P.n_prev ? t : P.n_prev - 1];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kSweep; ++k) {
+        const int t = t0 + k * NT;
+        if (t >= T) continue;
+        const double mq = double(w[k]) / wd;
+        const double c = t < P.n_prev ? double(cin[k]) * 0x1p-44 : floor(mq * 0x1p44) * 0x1p-44;
+        const double c_new = (P.lam * c) + (P.oml * mq);
+        const uint64_t cq = uint64_t(floor(c_new * 0x1p44));
+        cu[t] = cq;
+        part += cq;
+      }
+    }
+    const uint64_t c_total = block_sum_u64<NT>(part, sh);
+    const double cd = double(c_total);
+    for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
+      uint64_t w[kSweep], cq[kSweep];
+#pragma unroll
+      for (int k = 0; k < kSweep; ++k) {  // clamped loads (positions past T are skipped below)
+        const int t = t0 + k * NT;
+        w[k] = vn[t < T ? t : T - 1];
+        cq[k] = cu[t < T ? t : T - 1];
+      }
+#pragma unroll
+      for (int k = 0; k < kSweep; ++k) {
+        const int t = t0 + k * NT;
+        if (t >= T) continue;
+        const double mq = double(w[k]) / wd;
+        const double nc = c_total ? double(cq[k]) / cd : 0.0;
+        const double mix = (P.beta * mq) + (P.omb * nc);
+        vn[t] = uint64_t(floor(mix * 0x1p44));
+      }
+    }
+  }
+
+  if (T <= P.K) {  // nothing to evict
+    if (tid == 0) n_seg[n] = 0;
+    return;
+  }
+
+  // -- step 2d: inclusive prefix C(t) of v, in place (the sweeps above wrote
+  // v with another thread mapping)
+  __syncthreads();
+  {
+    uint64_t carry = 0;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int base = 0; base < T; base += NT * kScanItems) {
+      uint64_t x[kScanItems];
+      const int i0 = base + tid * kScanItems;
+#pragma unroll
+      for (int i = 0; i < kScanItems; ++i) x[i] = vn[i0 + i < T ? i0 + i : T - 1];
+#pragma unroll
+      for (int i = 0; i < kScanItems; ++i) x[i] = i0 + i < T ? x[i] : 0;
+#pragma unroll
+      for (int i = 1; i < kScanItems; ++i) x[i] += x[i - 1];
+      uint64_t incl = x[kScanItems - 1];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      __syncthreads();
+      if (lane == 63) sh.red_u64[wave] = incl;
+      __syncthreads();
+      uint64_t wave_off = 0, tile_total = 0;
+#pragma unroll
+      for (int i = 0; i < NT / 64; ++i) {
+        wave_off += i < wave ? sh.red_u64[i] : 0;
+        tile_total += sh.red_u64[i];
+      }
+      const uint64_t excl = carry + wave_off + (incl - x[kScanItems - 1]);
+#pragma unroll
+      for (int i = 0; i < kScanItems; ++i)
+        if (i0 + i < T) vn[i0 + i] = x[i] + excl;
+      carry += tile_total;
+    }
+  }
+  __syncthreads();
+  const uint64_t* Pn = vn;
+  const uint64_t V = Pn[T - 1];
+
+  // -- step 3b: thresholds theta_k = min(V, ceil(k*Delta*V)), cuts e_k
+  int32_t* en = ends + size_t(n) * (P.n_thr + 1);
+  for (int kk = tid; kk < P.n_thr; kk += NT) {
+    if (P.seg_fixed > 0) {  // ablation: a cut every seg_fixed positions
+      const int64_t e = int64_t(kk + 1) * P.seg_fixed - 1;
+      en[kk] = e < T - 1 ? int(e) : T - 1;  // cuts past the end collapse into T-1
+      continue;
+    }
+    const double x = ceil((double(kk + 1) * P.delta) * double(V));
+    uint64_t th = uint64_t(x);
+    if (th > V) th = V;
+    int lo = 0, hi = T - 1;  // P[T-1] = V >= th
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (Pn[mid] >= th) hi = mid; else lo = mid + 1;
+    }
+    en[kk] = lo;
+  }
+  __syncthreads();
+
+  // -- step 3c: raw segments (distinct cuts, plus T-1), greedy forward merge
+  if (tid == 0) {
+    int nm = 0, prev_end = -1;
+    int cur_a = -1, cur_b = -1;
+    for (int i = 0; i <= P.n_thr; ++i) {
+      const int e = i < P.n_thr ? en[i] : T - 1;
+      if (e <= prev_end) continue;  // equal cuts collapse; cuts are nondecreasing
+      const int a = prev_end + 1;
+      prev_end = e;
+      if (cur_a < 0) {
+        cur_a = a;
+        cur_b = e;
+      } else if (cur_b - cur_a + 1 < P.seg_min) {
+        cur_b = e;
+      } else {
+        sh.merged_a[nm] = cur_a;
+        sh.merged_b[nm] = cur_b;
+        ++nm;
+        cur_a = a;
+        cur_b = e;
+      }
+    }
+    if (cur_b - cur_a + 1 < P.seg_min && nm > 0) {
+      sh.merged_b[nm - 1] = cur_b;
+    } else {
+      sh.merged_a[nm] = cur_a;
+      sh.merged_b[nm] = cur_b;
+      ++nm;
+    }
+    // -- step 3d: pieces per merged segment
+    int off = 0;
+    for (int i = 0; i < nm; ++i) {
+      sh.piece_off[i] = off;
+      const int L = sh.merged_b[i] - sh.merged_a[i] + 1;
+      off += (P.seg_max > 0 && L > P.seg_max) ? (L + P.seg_max - 1) / P.seg_max : 1;
+    }
+    sh.piece_off[nm] = off;
+    sh.n_merged = nm;
+  }
+  __syncthreads();
+  const int nm = sh.n_merged;
+  const int ns = sh.piece_off[nm];  // <= s_cap by construction
+
+  // -- step 3e: per-segment length, must-keep overlap, mass, floor
+  const int s_end = mk.s - 1, r_beg = T - mk.r;
+  const size_t so = size_t(n) * P.s_cap;
+  int64_t f_part = 0;
+  uint64_t m_part = 0;
+  for (int s = tid; s < ns; s += NT) {
+    int lo = 0, hi = nm - 1;  // merged segment holding piece s
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sh.piece_off[mid] <= s) lo = mid; else hi = mid - 1;
+    }
+    const int a = sh.merged_a[lo], b = sh.merged_b[lo];
+    const int L = b - a + 1;
+    int start = a, len = L;
+    if (P.seg_max > 0 && L > P.seg_max) {
+      const int np = (L + P.seg_max - 1) / P.seg_max;
+      const int base = L / np, extra = L % np;
+      const int kq = s - sh.piece_off[lo];
+      start = a + kq * base + (kq < extra ? kq : extra);
+      len = base + (kq < extra ? 1 : 0);
+    }
+    const int end = start + len - 1;
+    const int kmk = overlap_len(start, end, 0, s_end) + overlap_len(start, end, r_beg, T - 1);
+    const int avail = len - kmk;
+    uint64_t mass = range_sum(Pn, start, end);
+    if (start <= s_end) mass -= range_sum(Pn, start, end < s_end ? end : s_end);
+    if (end >= r_beg) mass -= range_sum(Pn, start > r_beg ? start : r_beg, end);
+    const int lmin = P.q_min < len ? P.q_min : len;
+    int fl = lmin - kmk;
+    fl = fl < 0 ? 0 : fl;
+    fl = fl < avail ? fl : avail;
+    if (P.quota_uniform) mass = 1;  // ablation: every segment weighs the same
+    seg_start[so + s] = sp.off + start;
+    seg_m[so + s] = mass;
+    seg_a[so + s] = avail;
+    seg_f[so + s] = fl;
+    f_part += fl;
+    m_part += mass;
+  }
+  const int64_t F = block_sum_i64<NT>(f_part, sh);
+  const uint64_t SM = block_sum_u64<NT>(m_part, sh);
+
+  // -- step 3f/3g: quotas
+  if (F > mk.t_keep) {
+    for (int s = tid; s < ns; s += NT) seg_q[so + s] = seg_f[so + s];
+  } else {
+    const int64_t t_rem = mk.t_keep - F;
+    int64_t q_part = 0;
+    for (int s = tid; s < ns; s += NT) {
+      int64_t add = 0;
+      if (SM > 0) {
+        const double share = double(t_rem) * (double(seg_m[so + s]) / double(SM));
+        add = int64_t(floor(share + 0.5));
+      }
+      int64_t qv = seg_f[so + s] + add;
+      if (qv > seg_a[so + s]) qv = seg_a[so + s];
+      seg_q[so + s] = int32_t(qv);
+      q_part += qv;
+    }
+    const int64_t D = int64_t(mk.t_keep) - block_sum_i64<NT>(q_part, sh);
+    if (D != 0) {
+      // Cyclic walk in closed form: c full cycles give every segment
+      // min(room, c); the next, partial cycle gives one more to the first r
+      // segments (in walk order) whose room exceeds c.
+      const bool adding = D > 0;
+      const int64_t need = adding ? D : -D;
+      // Rooms and walk keys go to LDS when they fit (the ranks below read
+      // every segment once per segment).
+      const bool staged = ns <= Shared<NT>::kRankStage;
+      if (staged) {
+        for (int s = tid; s < ns; s += NT) {
+          sh.u.walk.room[s] = adding ? seg_a[so + s] - seg_q[so + s] : seg_q[so + s] - seg_f[so + s];
+          sh.u.walk.m[s] = seg_m[so + s];
+        }
+        __syncthreads();
+      }
+      auto room_of = [&](int s) -> int64_t {
+        if (staged) return sh.u.walk.room[s];
+        return adding ? seg_a[so + s] - seg_q[so + s] : seg_q[so + s] - seg_f[so + s];
+      };
+      auto m_of = [&](int s) -> uint64_t { return staged ? sh.u.walk.m[s] : seg_m[so + s]; };
+      int64_t rmax = 0;
+      for (int s = tid; s < ns; s += NT) {
+        const int64_t room = room_of(s);
+        rmax = room > rmax ? room : rmax;
+      }
+      rmax = block_max_i64<NT>(rmax, sh);
+      int64_t lo = 0, hi = rmax;
+      while (lo < hi) {  // largest c with sum min(room, c) <= need
+        const int64_t mid = (lo + hi + 1) >> 1;
+        int64_t sp = 0;
+        for (int s = tid; s < ns; s += NT) {
+          const int64_t room = room_of(s);
+          sp += room < mid ? room : mid;
+        }
+        if (block_sum_i64<NT>(sp, sh) <= need) lo = mid; else hi = mid - 1;
+      }
+      const int64_t cyc = lo;
+      int64_t sp = 0;
+      for (int s = tid; s < ns; s += NT) {
+        const int64_t room = room_of(s);
+        sp += room < cyc ? room : cyc;
+      }
+      const int64_t r = need - block_sum_i64<NT>(sp, sh);
+      // New quotas go to the output array; the ranks read the old rooms,
+      // which nothing writes during this loop.
+      for (int s = tid; s < ns; s += NT) {
+        const int64_t room = room_of(s);
+        int64_t delta = room < cyc ? room : cyc;
+        if (room > cyc && r > 0) {
+          const uint64_t ms = m_of(s);
+          int64_t rank = 0;
+          if (staged) {  // every thread reads the same entry: LDS broadcasts, no branches
+            int o = 0;
+            for (; o + 4 <= ns; o += 4)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                rank += (sh.u.walk.room[o + i] > cyc) &
+                        precedes(sh.u.walk.m[o + i], o + i, ms, s, adding);
+            for (; o < ns; ++o)
+              rank += (sh.u.walk.room[o] > cyc) & precedes(sh.u.walk.m[o], o, ms, s, adding);
+          } else {
+            for (int o = 0; o < ns && rank < r; ++o)
+              if (room_of(o) > cyc && precedes(m_of(o), o, ms, s, adding)) ++rank;
+          }
+          if (rank < r) ++delta;
+        }
+        seg_quota[so + s] = int32_t(adding ? seg_q[so + s] + delta : seg_q[so + s] - delta);
+      }
+      if (tid == 0) n_seg[n] = ns;
+      return;
+    }
+  }
+  __syncthreads();
+  for (int s = tid; s < ns; s += NT) seg_quota[so + s] = seg_q[so + s];
+  if (tid == 0) n_seg[n] = ns;
 }
 
 }  // namespace

@@ -1,9 +1,147 @@
-// Step 4 on gfx950: the stage kernel, one workgroup per head-event.  The
-// device code (and its sources) is in kvc_select_dev.h.
-#include "kvc_select_dev.h"
+// Step 4 on gfx950: in-segment top-q, union with must-keep, budget repair and
+// sorted kept indices.  One workgroup per head-event; the keep set lives as a
+// bitmap in LDS.
+//
+// Sources: AMS notes, key design 3 (last paragraph: union with the must-keep
+// set, duplicates counted once; over budget drop low-score non-must-keep
+// positions, under budget add high-score unselected ones) and key design 4
+// (per-segment top-k on the base score, kept indices sorted).
+//
+// Ranking is by (score desc, position asc).  Scores become order-preserving
+// 32-bit keys (+0 and -0 equal), so "the r best of a set" is exact integer
+// work: the largest key tau with at least r members >= tau (a bit-by-bit
+// search, one population count per bit), then the members above tau and the
+// lowest-positioned members equal to tau up to r.  The result is the unique
+// canonical selection, independent of thread order.
+#include "kvc_internal.h"
 
 namespace kvc {
 namespace {
+
+// Long caches run with 1024 threads per workgroup, short ones with 256.
+constexpr int kMaxWaves = 16;
+constexpr int kCached = 16;    // keys per thread kept in registers by the threshold search
+constexpr int kWaveSeg = 256;  // segments up to this length: one wave each
+constexpr int kPerLane = kWaveSeg / 64;
+
+// LDS of one workgroup of NT threads: the keep bitmap (the short-cache
+// variant only takes caches below 4096 positions, so its bitmap is small and
+// several workgroups share a CU) and, for that variant, the segment starts
+// and quotas when they fit (every thread reads each of them once per loop).
+template <int NT>
+struct Shared {
+  static constexpr int kBits = NT >= 1024 ? kMaxT / 32 : 4096 / 32;
+  static constexpr int kStage = NT >= 1024 ? 1 : 512;
+  uint32_t bits[kBits];
+  uint32_t red[kMaxWaves];
+  int32_t seg_s[kStage];
+  int32_t seg_q[kStage];
+};
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) == 0) return 0x80000000u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+template <class Sh>
+__device__ __forceinline__ bool test_bit(const Sh& sh, int t) {
+  return (sh.bits[t >> 5] >> (t & 31)) & 1u;
+}
+
+template <class Sh>
+__device__ __forceinline__ void set_bit(Sh& sh, int t) {
+  atomicOr(&sh.bits[t >> 5], 1u << (t & 31));
+}
+
+template <class Sh>
+__device__ __forceinline__ void clear_bit(Sh& sh, int t) {
+  atomicAnd(&sh.bits[t >> 5], ~(1u << (t & 31)));
+}
+
+// Block-wide count; every thread must call it.
+template <int NT>
+__device__ uint32_t block_count(uint32_t c, Shared<NT>& sh) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += sh.red[i];
+  return s;
+}
+
+// The r best positions of {t in [a,b] : pred(t)} are those with key > tau,
+// plus those with key == tau and t <= xcut.  Requires 1 <= r < |set|; every
+// thread must call it with the same arguments.  tau is found bit by bit (the
+// largest key with at least r members >= it), xcut by a binary search over
+// positions.  When the range fits, each thread first caches its candidates'
+// keys in registers (kCached per thread), so the 32 + log2(L) counting rounds
+// read no memory; otherwise they re-read the scores.
+template <int NT, class Pred>
+__device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint32_t r, Pred pred,
+                                Shared<NT>& sh, uint32_t* tau_out, int* xcut_out) {
+  uint32_t tau = 0;
+  int lo = a, hi = b;
+  if (b - a + 1 <= NT * kCached) {
+    uint32_t key[kCached];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int i = 0; i < kCached; ++i) {  // clamped loads: all issued before any is used
+      const int t = a + int(threadIdx.x) + i * NT;
+      const float x = sc[t <= b ? t : b];
+      const bool ok = t <= b && pred(t);
+      key[i] = ok ? order_key(x) : 0u;
+      valid |= ok ? (1u << i) : 0u;
+    }
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < kCached; ++i) c += ((valid >> i) & 1u) && key[i] >= cand ? 1u : 0u;
+      if (block_count<NT>(c, sh) >= r) tau = cand;
+    }
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < kCached; ++i) c += ((valid >> i) & 1u) && key[i] > tau ? 1u : 0u;
+    const uint32_t need = r - block_count<NT>(c, sh);
+    while (lo < hi) {
+      const int mid = lo + ((hi - lo) >> 1);
+      uint32_t e = 0;
+#pragma unroll
+      for (int i = 0; i < kCached; ++i) {
+        const int t = a + int(threadIdx.x) + i * NT;
+        e += ((valid >> i) & 1u) && t <= mid && key[i] == tau ? 1u : 0u;
+      }
+      if (block_count<NT>(e, sh) >= need) hi = mid; else lo = mid + 1;
+    }
+  } else {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      uint32_t c = 0;
+      for (int t = a + threadIdx.x; t <= b; t += NT)
+        c += (pred(t) && order_key(sc[t]) >= cand) ? 1u : 0u;
+      if (block_count<NT>(c, sh) >= r) tau = cand;
+    }
+    uint32_t c = 0;
+    for (int t = a + threadIdx.x; t <= b; t += NT)
+      c += (pred(t) && order_key(sc[t]) > tau) ? 1u : 0u;
+    const uint32_t need = r - block_count<NT>(c, sh);
+    while (lo < hi) {
+      const int mid = lo + ((hi - lo) >> 1);
+      uint32_t e = 0;
+      for (int t = a + threadIdx.x; t <= mid; t += NT)
+        e += (pred(t) && order_key(sc[t]) == tau) ? 1u : 0u;
+      if (block_count<NT>(e, sh) >= need) hi = mid; else lo = mid + 1;
+    }
+  }
+  *tau_out = tau;
+  *xcut_out = lo;
+}
+
+__device__ __forceinline__ uint32_t wave_count(bool v) { return __popcll(__ballot(v)); }
 
 template <int NT>
 __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restrict__ score,
@@ -11,8 +149,205 @@ __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restric
                                                      const int32_t* __restrict__ seg_quota,
                                                      const int32_t* __restrict__ n_seg,
                                                      int32_t* __restrict__ kept) {
-  __shared__ sel::Shared<NT> sh;
-  sel::select_head<NT>(P, int(blockIdx.x), score, seg_start, seg_quota, n_seg, kept, sh);
+  __shared__ Shared<NT> sh;
+  const int n = blockIdx.x;
+  // A left-padded head runs on its real tokens [off, off + T) only; kept
+  // holds positions of the padded cache.
+  const Span sp = head_span(P, n);
+  const int T = sp.T, K = P.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* kn = kept + size_t(n) * K;
+  if (T <= K) {  // nothing to evict: identity, -1 past T
+    for (int j = tid; j < K; j += NT) kn[j] = j < T ? sp.off + j : -1;
+    return;
+  }
+  const float* sc = score + size_t(n) * P.T + sp.off;
+  const int nw = (T + 31) >> 5;
+  const Keep mk = P.vlen ? must_keep(P.sinks, P.recent, P.K, T) : Keep{P.s_keep, P.r_keep, P.t_keep};
+  const int s_keep = mk.s, r_beg = T - mk.r;
+  auto must_keep = [&](int t) { return t < s_keep || t >= r_beg; };
+
+  // Segments as given (sanitised to [0,T); empty ones are skipped).
+  int ns = n_seg[n];
+  ns = ns < 0 ? 0 : (ns > P.s_cap ? P.s_cap : ns);
+  const int32_t* ss = seg_start + size_t(n) * P.s_cap;
+  const int32_t* sq = seg_quota + size_t(n) * P.s_cap;
+  const bool staged = NT < 1024 && ns <= Shared<NT>::kStage;
+  for (int w = tid; w < nw; w += NT) sh.bits[w] = 0;
+  if (staged)
+    for (int i = tid; i < ns; i += NT) {
+      sh.seg_s[i] = ss[i];
+      sh.seg_q[i] = sq[i];
+    }
+  __syncthreads();
+  for (int t = tid; t < s_keep; t += NT) set_bit(sh, t);
+  for (int t = r_beg + tid; t < T; t += NT) set_bit(sh, t);
+  auto start_of = [&](int i) { return staged ? sh.seg_s[i] : ss[i]; };
+  auto quota_of = [&](int i) {
+    const int q = staged ? sh.seg_q[i] : sq[i];
+    return q < 0 ? 0 : q;
+  };
+  auto seg_bounds = [&](int i, int* a, int* b) {  // starts are padded-cache positions
+    int s0 = start_of(i) - sp.off, s1 = i + 1 < ns ? start_of(i + 1) - sp.off : T;
+    s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
+    s1 = s1 < 0 ? 0 : (s1 > T ? T : s1);
+    *a = s0;
+    *b = s1 - 1;
+  };
+
+  // Long segments: the whole workgroup, one at a time.
+  for (int i = 0; i < ns; ++i) {
+    int a, b;
+    seg_bounds(i, &a, &b);
+    if (b - a + 1 <= kWaveSeg) continue;
+    const int q = quota_of(i);
+    uint32_t c = 0;
+    for (int t = a + tid; t <= b; t += NT) c += must_keep(t) ? 0u : 1u;
+    const uint32_t avail = block_count<NT>(c, sh);
+    if (q == 0 || avail == 0) continue;
+    if (uint32_t(q) >= avail) {
+      for (int t = a + tid; t <= b; t += NT)
+        if (!must_keep(t)) set_bit(sh, t);
+      continue;
+    }
+    uint32_t tau;
+    int xcut;
+    block_threshold<NT>(sc, a, b, uint32_t(q), [&](int t) { return !must_keep(t); }, sh, &tau, &xcut);
+    for (int t = a + tid; t <= b; t += NT) {
+      if (must_keep(t)) continue;
+      const uint32_t kk = order_key(sc[t]);
+      if (kk > tau || (kk == tau && t <= xcut)) set_bit(sh, t);
+    }
+  }
+
+  // Short segments: one wave each, keys held in registers.
+  for (int i = wave; i < ns; i += (NT / 64)) {
+    int a, b;
+    seg_bounds(i, &a, &b);
+    const int L = b - a + 1;
+    if (L <= 0 || L > kWaveSeg) continue;
+    const int q = quota_of(i);
+    if (q == 0) continue;
+    bool ok[kPerLane];
+    uint32_t key[kPerLane];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) {  // clamped loads: all issued before any is used
+      const int t = a + lane + 64 * e;
+      const float x = sc[t <= b ? t : b];
+      ok[e] = t <= b && !must_keep(t);
+      key[e] = ok[e] ? order_key(x) : 0u;
+      avail += wave_count(ok[e]);
+    }
+    if (uint32_t(q) >= avail) {
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e)
+        if (ok[e]) set_bit(sh, a + lane + 64 * e);
+      continue;
+    }
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) c += wave_count(ok[e] && key[e] >= cand);
+      if (c >= uint32_t(q)) tau = cand;
+    }
+    uint32_t gt = 0;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) gt += wave_count(ok[e] && key[e] > tau);
+    const uint32_t need = uint32_t(q) - gt;
+    // Positions a+lane+64e in ascending order are e-major, lane-minor: walk
+    // the ties in that order and take the first `need`.
+    uint32_t taken = 0;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) {
+      const bool tie = ok[e] && key[e] == tau;
+      const uint64_t m = __ballot(tie);
+      const uint32_t before = __popcll(m & ((uint64_t(1) << lane) - 1));
+      const bool take = ok[e] && (key[e] > tau || (tie && taken + before < need));
+      if (take) set_bit(sh, a + lane + 64 * e);
+      taken += __popcll(m);
+    }
+  }
+  __syncthreads();
+
+  // Budget repair.
+  uint32_t c = 0;
+  for (int w = tid; w < nw; w += NT) c += __popc(sh.bits[w]);
+  const uint32_t n_keep = block_count<NT>(c, sh);
+  const uint32_t n_mk = uint32_t(mk.s + mk.r);
+  if (n_keep > uint32_t(K)) {
+    // Keep the best K - |MK| picks, drop the rest (the lowest-scored first).
+    auto is_pick = [&](int t) { return !must_keep(t) && test_bit(sh, t); };
+    const uint32_t r = uint32_t(K) - n_mk;
+    if (r == 0) {
+      __syncthreads();
+      for (int t = tid; t < T; t += NT)
+        if (!must_keep(t)) clear_bit(sh, t);
+    } else {
+      uint32_t tau;
+      int xcut;
+      block_threshold<NT>(sc, 0, T - 1, r, is_pick, sh, &tau, &xcut);
+      // Each thread tests and clears only its own positions' bits.
+      __syncthreads();
+      for (int t = tid; t < T; t += NT) {
+        if (must_keep(t) || !test_bit(sh, t)) continue;
+        const uint32_t kk = order_key(sc[t]);
+        if (!(kk > tau || (kk == tau && t <= xcut))) clear_bit(sh, t);
+      }
+    }
+  } else if (n_keep < uint32_t(K)) {
+    // Add the best unselected positions.
+    auto is_free = [&](int t) { return !must_keep(t) && !test_bit(sh, t); };
+    const uint32_t r = uint32_t(K) - n_keep;
+    uint32_t f = 0;
+    for (int t = tid; t < T; t += NT) f += is_free(t) ? 1u : 0u;
+    const uint32_t n_free = block_count<NT>(f, sh);
+    if (r >= n_free) {
+      __syncthreads();
+      for (int t = tid; t < T; t += NT)
+        if (!must_keep(t)) set_bit(sh, t);
+    } else {
+      uint32_t tau;
+      int xcut;
+      block_threshold<NT>(sc, 0, T - 1, r, is_free, sh, &tau, &xcut);
+      // Each thread tests and sets only its own positions' bits.
+      __syncthreads();
+      for (int t = tid; t < T; t += NT) {
+        if (!is_free(t)) continue;
+        const uint32_t kk = order_key(sc[t]);
+        if (kk > tau || (kk == tau && t <= xcut)) set_bit(sh, t);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Compaction: ascending positions of the set bits.
+  const int wpt = (nw + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  uint32_t cnt = 0;
+  for (int w = w0; w < w0 + wpt && w < nw; ++w) cnt += __popc(sh.bits[w]);
+  uint32_t incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) sh.red[wave] = incl;
+  __syncthreads();
+  uint32_t pos = incl - cnt;
+  for (int i = 0; i < wave; ++i) pos += sh.red[i];
+  for (int w = w0; w < w0 + wpt && w < nw; ++w) {
+    uint32_t word = sh.bits[w];
+    while (word) {
+      const int b = __ffs(word) - 1;
+      word &= word - 1;
+      if (pos < uint32_t(K)) kn[pos] = sp.off + w * 32 + b;
+      ++pos;
+    }
+  }
 }
 
 }  // namespace
