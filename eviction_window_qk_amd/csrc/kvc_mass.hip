@@ -423,7 +423,53 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   const int64_t F = block_sum_i64<NT>(f_part, sh);
   const uint64_t SM = block_sum_u64<NT>(m_part, sh);
 
-  // -- step 3f/3g: quotas
+  // -- step 3f/3g: quotas.  Up to 64 segments (the common case) one wave does
+  // it alone, lane s holding segment s (written by this same thread in 3e),
+  // with wave reductions instead of block-wide ones; the arithmetic is the
+  // same as the block-wide version below.
+  if (ns <= 64) {
+    if (tid < 64) {
+      const int s = tid;
+      const bool has = s < ns;
+      const int64_t fl = has ? seg_f[so + s] : 0, av = has ? seg_a[so + s] : 0;
+      const uint64_t ms = has ? seg_m[so + s] : 0;
+      int64_t qv = fl;
+      if (F <= mk.t_keep) {
+        const int64_t t_rem = mk.t_keep - F;
+        int64_t add = 0;
+        if (has && SM > 0) {
+          const double share = double(t_rem) * (double(ms) / double(SM));
+          add = int64_t(floor(share + 0.5));
+        }
+        qv = fl + add < av ? fl + add : av;
+        const int64_t D = int64_t(mk.t_keep) - wave_sum_i64(qv);
+        if (D != 0) {  // the cyclic walk in closed form, as below
+          const bool adding = D > 0;
+          const int64_t need = adding ? D : -D;
+          const int64_t room = has ? (adding ? av - qv : qv - fl) : 0;
+          int64_t lo = 0, hi = wave_max_i64(room);
+          while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (wave_sum_i64(room < mid ? room : mid) <= need) lo = mid; else hi = mid - 1;
+          }
+          const int64_t cyc = lo;
+          const int64_t r = need - wave_sum_i64(room < cyc ? room : cyc);
+          int64_t delta = room < cyc ? room : cyc;
+          int64_t rank = 0;
+          for (int o = 0; o < ns; ++o) {  // every lane walks all segments (uniform)
+            const int64_t ro = __shfl(room, o);
+            const uint64_t mo = __shfl(ms, o);
+            rank += (ro > cyc) & precedes(mo, o, ms, s, adding);
+          }
+          if (room > cyc && rank < r) ++delta;
+          qv = adding ? qv + delta : qv - delta;
+        }
+      }
+      if (has) seg_quota[so + s] = int32_t(qv);
+      if (s == 0) n_seg[n] = ns;
+    }
+    return;
+  }
   if (F > mk.t_keep) {
     for (int s = tid; s < ns; s += NT) seg_q[so + s] = seg_f[so + s];
   } else {
