@@ -108,6 +108,10 @@ class Params:
         return self.t_stride or self.T
 
 
+# The kvc_params layout and entry-point signatures this binding marshals
+# (KVC_ABI_VERSION in include/kvc.h); a library of another version is refused.
+ABI_VERSION = 2
+
 _lib = None
 
 
@@ -149,6 +153,9 @@ def lib() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     L.kvc_workspace_bytes.restype = ctypes.c_size_t
     L.kvc_strerror.restype = ctypes.c_char_p
+    if L.kvc_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {L.kvc_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild with `python -m eviction_window_qk_amd.build`")
     _lib = L
     return L
 

@@ -5,6 +5,7 @@ import ctypes
 import subprocess
 import os
 import re
+import sys
 
 import pytest
 
@@ -42,10 +43,22 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert kvc.abi_version() == 2
+    assert kvc.abi_version() == kvc.ABI_VERSION == 2
     for code in (0, 1, -1, -2, -3, -4, -5):
         assert kvc.strerror(code) and kvc.strerror(code) != "unknown status"
     assert kvc.strerror(-99) == "unknown status"
+
+
+def test_header_version_matches_binding():
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+KVC_ABI_VERSION\s+(\d+)", src)
+    assert m and int(m.group(1)) == kvc.ABI_VERSION
+
+
+def test_graft_entry_import_check():
+    sys.path.insert(0, ROOT)
+    import __graft_entry__
+    __graft_entry__.check_import()
 
 
 def test_param_struct_layout(tmp_path):
