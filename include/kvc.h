@@ -84,9 +84,12 @@ typedef struct kvc_params {
   int32_t n_heads;     /* NH independent head-events; 0 = nothing to do      */
   int32_t group;       /* G query heads per KV head, 1..64                   */
   int32_t head_dim;    /* d, 64 or 128                                       */
-  int32_t T;           /* valid cached positions per head, 1..2^20           */
+  int32_t T;           /* valid cached positions per head, 1..2^18           */
   int32_t t_stride;    /* rows allocated per head in k/v (>= T)              */
-  int32_t window;      /* W recent queries, 1..T, W*G <= 4096                */
+  int32_t window;      /* W recent queries, 1..T; W*G <= 4096 and
+                          G*ceil(W/32)*32 <= 4096 (32-row MFMA blocks per
+                          query head); 7*W*W*G < 2^22 keeps the fixed-point
+                          usage totals below 2^63                            */
   int32_t budget;      /* K positions kept per head, >= 1                    */
   int32_t seg_min;     /* shortest segment after merging (>= 1), e.g. 16     */
   int32_t seg_max;     /* longest segment after splitting, e.g. 256; 0 = none*/
@@ -271,9 +274,10 @@ int kvc_compress_event(const kvc_params* p, const void* q_win, const void* k, co
  * the parameters are invalid).  Pure host function. */
 size_t kvc_workspace_bytes(const kvc_params* p);
 
-/* Segment capacity S per head: n_thr + 1 + floor(T/seg_max) capped at T,
- * with n_thr = #{k >= 1 : k*delta < 1}; seg_max = 0 drops the second term.
- * Returns a negative status for invalid parameters.  Pure host function. */
+/* Segment capacity S per head: n_cut + 1 + floor(T/seg_max) capped at T,
+ * with n_cut = #{k >= 1 : k*delta < 1} (or ceil(T/seg_fixed) - 1 with fixed
+ * segments); seg_max = 0 drops the second term.  Returns a negative status
+ * for invalid parameters.  Pure host function. */
 int kvc_segment_capacity(const kvc_params* p);
 
 /* Validates the parameters alone (no pointers): KVC_OK or the error code.
