@@ -96,18 +96,34 @@ def algorithmic(wl, lengths=None) -> dict:
                 b_gather=b_gather, b_total=b_score + b_mass + b_select + b_gather)
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per score-stage launch from the committed counter runs
-    (profiles/traffic_<workload>.json), or None when the score kernels have
-    changed since the counters were taken (source hash mismatch)."""
+def _recorded(kind: str, workload: str):
+    """A committed counter record (profiles/<kind>_<workload>.json), or None
+    when it is missing or the score kernels have changed since the counters
+    were taken (source hash mismatch)."""
     import hashlib
-    f = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    f = os.path.join(ROOT, "profiles", f"{kind}_{workload}.json")
     if not os.path.exists(f):
         return None
     rec = json.load(open(f))
     src = os.path.join(ROOT, "eviction_window_qk_amd", "csrc", "kvc_score.hip")
     h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return rec["score_stage_traffic_bytes"] if rec.get("score_source_sha256_16") == h else None
+    return rec if rec.get("score_source_sha256_16") == h else None
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per score-stage launch (FETCH_SIZE + WRITE_SIZE runs)."""
+    rec = _recorded("traffic", workload)
+    return rec["score_stage_traffic_bytes"] if rec else None
+
+
+def recorded_mfma(workload: str):
+    """rocprofv3 MfmaUtil of the two score passes and the bf16 flops they
+    execute per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)."""
+    rec = _recorded("mfma", workload)
+    if not rec:
+        return None
+    return {"mfma_busy": rec["mfma_busy"],
+            "executed_flops_per_launch": sum(rec["mfma_flops_per_launch"].values())}
 
 
 def _oracle_head(args):
@@ -416,6 +432,12 @@ def main():
                       "select": stage_ms[2], "gather": stage_ms[3]},
         "gather": {"achieved_GBs": gather_gbs, "frac": gather_gbs / PEAK_HBM_GBS},
     }
+    mf = None if (args.ragged or variant) else recorded_mfma(wl.name)
+    if mf:  # counter-derived, from profiles/: executed work (two passes) and MFMA busy
+        ex = mf["executed_flops_per_launch"] / (score_ms * 1e-3) / 1e12
+        line["roofline"].update({"executed_flops_per_launch": mf["executed_flops_per_launch"],
+                                 "executed_frac": ex / PEAK_BF16_TFLOPS,
+                                 "mfma_busy": mf["mfma_busy"]})
     if paged:
         line["paged_gather"] = paged
     if not args.no_cpu_baseline and not (args.ragged or variant):
