@@ -261,7 +261,15 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": args.copy_probe}))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        secs = e0.elapsed_time(e1) / 10 * 1e-3
+        print(json.dumps({"copy_probe_bytes": args.copy_probe,
+                          "copy_read_plus_write_GBs": 2 * args.copy_probe / secs / 1e9}))
         return
     wl = synth.WORKLOADS[args.workload]
     if args.refresh:
