@@ -1,0 +1,44 @@
+"""GPU parity at the limits the host accepts (include/kvc.h): the longest
+cache (2^18 positions), the most query rows per KV head (W*G = 4096, G = 64),
+the most mass thresholds (1024) and the most fixed segments (1025) -- the
+last two also take the segment tables past what the workgroups stage in LDS,
+so the global-memory fallbacks of the quota walk and of select run.  Same
+acceptance as tests/test_gpu_parity.py: usage within 2e-3 of the fp64 oracle,
+steps 2-5 bit for bit on the oracle's usage, the event equal to the stages."""
+import pytest
+
+from eviction_window_qk_amd import kvc, synth
+from test_gpu_parity import _pd, _run_case
+
+LIMITS = [
+    # (label, NH, G, W, d, T, K, overrides)
+    ("max_T", 1, 1, 4, 64, 1 << 18, 4096, {}),
+    ("max_rows_G64_W64", 2, 64, 64, 128, 1024, 300, {}),
+    ("G64_W1", 2, 64, 1, 64, 700, 100, {}),
+    ("max_thresholds", 1, 2, 16, 64, 8192, 2000, dict(delta=1.0 / 1025, seg_min=1, seg_max=0)),
+    # q_min = 0: no floors, so the quota walk runs over all 1025 segments
+    ("max_fixed_segments", 1, 2, 16, 64, 2050, 600, dict(seg_fixed=2, seg_min=1, seg_max=0,
+                                                        q_min=0)),
+    # about 4100 segments: past what the 1024-thread workgroup stages in LDS
+    ("max_T_many_segments", 1, 1, 4, 64, 1 << 18, 8192, dict(seg_max=64)),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", LIMITS, ids=[c[0] for c in LIMITS])
+def test_limits(case):
+    label, NH, G, W, d, T, K, over = case
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K, **over)
+    assert kvc.check_params(kvc.Params(n_heads=NH, T=T, window=W, budget=K, group=G, head_dim=d,
+                                       **{k: v for k, v in over.items()})) == 0
+    q, k, v = synth.random_small(sum(map(ord, label)), NH, G, W, d, T)
+    _run_case(pd, q, k, v, label=label)
+
+
+def test_segment_counts_reach_the_limits():
+    """The two segment-count cases really produce 1025 segments."""
+    from oracle import ams
+    p = ams.Params(T=2050, window=16, budget=600, seg_fixed=2, seg_min=1, seg_max=0, q_min=0)
+    assert ams.segment_capacity(p) == 1025
+    p = ams.Params(T=8192, window=16, budget=2000, delta=1.0 / 1025, seg_min=1, seg_max=0)
+    assert ams.segment_capacity(p) == 1025
