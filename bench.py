@@ -243,7 +243,7 @@ def main():
                          "blocks of a shuffled pool, driven by the event's kept indices")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (the event is independent per head "
+        print(f"bench.py: measures one GPU only (the event is independent per head "
               f"and runs on one GPU's share); --gpus {args.gpus} is not supported",
               file=sys.stderr)
         sys.exit(2)

@@ -1,6 +1,6 @@
 """The counter records bench.py attaches to its line (profiles/*.json) match the
-committed score source, and the bench's algorithmic counts agree with the
-survey's per-config figures (CPU only)."""
+committed score source, and the bench's algorithmic flop counts agree with the
+closed form of one causal QK^T, 2*d*G*(W(T-W) + W(W+1)/2) per head (CPU only)."""
 import os
 import sys
 
@@ -31,5 +31,6 @@ def test_executed_flops_cover_two_passes():
 @pytest.mark.parametrize("name,flops", [("qwen7b_t768", 289.6e9), ("qwen7b_t1536_ema", 2.421e12),
                                         ("llama8b_global_t16k", 549.2e9),
                                         ("llama8b_t128k", 4.396e12)])
-def test_algorithmic_flops_match_survey(name, flops):
+def test_algorithmic_flops_match_closed_form(name, flops):
+    # NH * 2*d*G*(W(T-W) + W(W+1)/2) for each workload's shape
     assert bench.algorithmic(synth.WORKLOADS[name])["flops"] == pytest.approx(flops, rel=2e-3)
