@@ -32,8 +32,13 @@ template <int NT>
 struct Shared {
   static constexpr int kBits = NT >= 1024 ? kMaxT / 32 : 4096 / 32;
   static constexpr int kStage = NT >= 1024 ? 1 : 512;
+  // Segments longer than kWaveSeg cover more than 256 positions each: at most
+  // T/257 of them (15 below 4096 positions, 1020 at 2^18).
+  static constexpr int kLongCap = NT >= 1024 ? 1024 : 16;
   uint32_t bits[kBits];
   uint32_t red[kMaxWaves];
+  int32_t long_ids[kLongCap];
+  int n_long;
   int32_t seg_s[kStage];
   int32_t seg_q[kStage];
 };
@@ -203,11 +208,25 @@ __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restric
     *b = s1 - 1;
   };
 
-  // Long segments: the whole workgroup, one at a time.
-  for (int i = 0; i < ns; ++i) {
+  // Long segments: the whole workgroup, one at a time.  They are few, so
+  // the threads first list them together (in any order: each one only sets
+  // bits of its own range) instead of every wave scanning all segments.
+  if (tid == 0) sh.n_long = 0;
+  __syncthreads();
+  for (int i = tid; i < ns; i += NT) {
     int a, b;
     seg_bounds(i, &a, &b);
-    if (b - a + 1 <= kWaveSeg) continue;
+    if (b - a + 1 > kWaveSeg) {
+      const int slot = atomicAdd(&sh.n_long, 1);
+      if (slot < Shared<NT>::kLongCap) sh.long_ids[slot] = i;
+    }
+  }
+  __syncthreads();
+  const int n_long = sh.n_long < Shared<NT>::kLongCap ? sh.n_long : Shared<NT>::kLongCap;
+  for (int li = 0; li < n_long; ++li) {
+    const int i = sh.long_ids[li];
+    int a, b;
+    seg_bounds(i, &a, &b);
     const int q = quota_of(i);
     uint32_t c = 0;
     for (int t = a + tid; t <= b; t += NT) c += must_keep(t) ? 0u : 1u;
