@@ -156,6 +156,18 @@ __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint
 
 __device__ __forceinline__ uint32_t wave_count(bool v) { return __popcll(__ballot(v)); }
 
+// Minimum over the wave's 64 lanes, uniform result (DPP within 16-lane rows,
+// then the four row minima read back).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0xb1, 0xf, 0xf, false)));
+  x = min(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0x4e, 0xf, 0xf, false)));
+  x = min(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0x141, 0xf, 0xf, false)));
+  x = min(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0x140, 0xf, 0xf, false)));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return min(min(a, b), min(c, d));
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restrict__ score,
                                                      const int32_t* __restrict__ seg_start,
@@ -272,13 +284,30 @@ __global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restric
         if (ok[e]) set_bit(sh, a + lane + 64 * e);
       continue;
     }
+    // tau: the largest key with at least q members >= it, bit by bit.  Once
+    // exactly q members are >= the candidate, tau is their smallest key and
+    // the remaining bits need no counting.
     uint32_t tau = 0;
+    bool exact = false;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = tau | (1u << bit);
       uint32_t c = 0;
 #pragma unroll
       for (int e = 0; e < kPerLane; ++e) c += wave_count(ok[e] && key[e] >= cand);
-      if (c >= uint32_t(q)) tau = cand;
+      if (c >= uint32_t(q)) {
+        tau = cand;
+        if (c == uint32_t(q)) {
+          exact = true;
+          break;
+        }
+      }
+    }
+    if (exact) {
+      uint32_t mn = 0xffffffffu;
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e)
+        if (ok[e] && key[e] >= tau) mn = key[e] < mn ? key[e] : mn;
+      tau = wave_min_u32(mn);
     }
     uint32_t gt = 0;
 #pragma unroll
