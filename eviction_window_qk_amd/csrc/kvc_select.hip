@@ -9,10 +9,10 @@
 //
 // Ranking is by (score desc, position asc).  Scores become order-preserving
 // 32-bit keys (+0 and -0 equal), so "the r best of a set" is exact integer
-// work: the largest key tau with at least r members >= tau (a bit-by-bit
-// search, one population count per bit), then the members above tau and the
-// lowest-positioned members equal to tau up to r.  The result is the unique
-// canonical selection, independent of thread order.
+// work: the largest key tau with at least r members >= tau (found digit by
+// digit with histograms, or bit by bit with population counts), then the
+// members above tau and the lowest-positioned members equal to tau up to r.
+// The result is the unique canonical selection, independent of thread order.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -41,6 +41,18 @@ struct Shared {
   int n_long;
   int32_t seg_s[kStage];
   int32_t seg_q[kStage];
+  // Radix threshold search over register-cached keys.  The 256-bin digit
+  // histogram is kept in kCopies copies (bin-major, the copy picked by the
+  // thread index), folded into hsum after each round: the leading digit of
+  // a float key is its sign and high exponent bits, so most of a wave's
+  // keys share a bin, and one copy would serialise their LDS atomics (eight
+  // copies measured 2x faster on a 16K-position cache).  Then the chosen
+  // digit and count, and per (cached slot, wave) the ballot of ties.
+  static constexpr int kCopies = NT >= 1024 ? 8 : 4;
+  uint32_t hist[256 * kCopies];
+  uint32_t hsum[256];
+  uint32_t pick[2];
+  uint64_t tie_mask[kCached * (NT / 64)];
 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -88,11 +100,12 @@ __device__ uint32_t block_count(uint32_t c, Shared<NT>& sh) {
 
 // The r best positions of {t in [a,b] : pred(t)} are those with key > tau,
 // plus those with key == tau and t <= xcut.  Requires 1 <= r < |set|; every
-// thread must call it with the same arguments.  tau is found bit by bit (the
-// largest key with at least r members >= it), xcut by a binary search over
-// positions.  When the range fits, each thread first caches its candidates'
-// keys in registers (kCached per thread), so the 32 + log2(L) counting rounds
-// read no memory; otherwise they re-read the scores.
+// thread must call it with the same arguments.  tau is the largest key with
+// at least r members >= it.  When the range fits, each thread caches its
+// candidates' keys in registers (kCached per thread); tau then takes four
+// rounds of an 8-bit-digit histogram and xcut one pass over per-wave ballots
+// of the ties.  Otherwise tau is found bit by bit and xcut by a binary search
+// over positions, each step one block-wide count that re-reads the scores.
 template <int NT, class Pred>
 __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint32_t r, Pred pred,
                                 Shared<NT>& sh, uint32_t* tau_out, int* xcut_out) {
@@ -109,27 +122,108 @@ __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint
       key[i] = ok ? order_key(x) : 0u;
       valid |= ok ? (1u << i) : 0u;
     }
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tau | (1u << bit);
-      uint32_t c = 0;
+    // tau, eight bits at a time: histogram the digit of the members whose
+    // higher digits equal tau's so far, then take the largest digit d with
+    // (members above) + (members with digit >= d) >= r.  `above` counts the
+    // members already known to be > tau.
+    constexpr int kC = Shared<NT>::kCopies;
+    const uint32_t copy = threadIdx.x % kC;
+    uint32_t above = 0;
+    for (int i = int(threadIdx.x); i < 256 * kC; i += NT) sh.hist[i] = 0;
+    __syncthreads();
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      const uint32_t hi_mask = shift == 24 ? 0u : (0xffffffffu << (shift + 8));
 #pragma unroll
-      for (int i = 0; i < kCached; ++i) c += ((valid >> i) & 1u) && key[i] >= cand ? 1u : 0u;
-      if (block_count<NT>(c, sh) >= r) tau = cand;
-    }
-    uint32_t c = 0;
+      for (int i = 0; i < kCached; ++i)
+        if (((valid >> i) & 1u) && (key[i] & hi_mask) == tau)
+          atomicAdd(&sh.hist[((key[i] >> shift) & 255u) * kC + copy], 1u);
+      __syncthreads();
+      for (int d = int(threadIdx.x); d < 256; d += NT) {  // fold the copies, clear them for the next round
+        uint32_t v = 0;
 #pragma unroll
-    for (int i = 0; i < kCached; ++i) c += ((valid >> i) & 1u) && key[i] > tau ? 1u : 0u;
-    const uint32_t need = r - block_count<NT>(c, sh);
-    while (lo < hi) {
-      const int mid = lo + ((hi - lo) >> 1);
-      uint32_t e = 0;
-#pragma unroll
-      for (int i = 0; i < kCached; ++i) {
-        const int t = a + int(threadIdx.x) + i * NT;
-        e += ((valid >> i) & 1u) && t <= mid && key[i] == tau ? 1u : 0u;
+        for (int c = 0; c < kC; ++c) {
+          v += sh.hist[d * kC + c];
+          sh.hist[d * kC + c] = 0;
+        }
+        sh.hsum[d] = v;
       }
-      if (block_count<NT>(e, sh) >= need) hi = mid; else lo = mid + 1;
+      __syncthreads();
+      if (threadIdx.x < 64) {  // lane l holds digits 4l .. 4l+3
+        const int l = int(threadIdx.x);
+        const uint32_t h0 = sh.hsum[4 * l], h1 = sh.hsum[4 * l + 1], h2 = sh.hsum[4 * l + 2],
+                       h3 = sh.hsum[4 * l + 3];
+        uint32_t suf = h0 + h1 + h2 + h3;  // inclusive suffix sum over lanes l..63
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_down(suf, off);
+          if (l + off < 64) suf += y;
+        }
+        // members with digit >= 4l+3, 4l+2, 4l+1, 4l
+        const uint32_t c3 = suf - h0 - h1 - h2, c2 = c3 + h2, c1 = c2 + h1, c0 = suf;
+        int d = -1;
+        uint32_t gt = 0;  // members with digit > d
+        if (above + c0 >= r) { d = 4 * l; gt = c1; }
+        if (above + c1 >= r) { d = 4 * l + 1; gt = c2; }
+        if (above + c2 >= r) { d = 4 * l + 2; gt = c3; }
+        if (above + c3 >= r) { d = 4 * l + 3; gt = c3 - h3; }
+        const uint64_t m = __ballot(d >= 0);  // lanes with a qualifying digit
+        const int top = 63 - __clzll(m);      // the largest digits live in the highest lane
+        if (l == top) {
+          sh.pick[0] = uint32_t(d);
+          sh.pick[1] = above + gt;
+        }
+      }
+      __syncthreads();
+      tau |= sh.pick[0] << shift;
+      above = sh.pick[1];
     }
+    // xcut: the need-th tie (key == tau) in ascending position order, i.e.
+    // slot-major, then thread order; ties are counted per (slot, wave).
+    const uint32_t need = r - above;
+    constexpr int kW = NT / 64;
+    const int lane = int(threadIdx.x) & 63, wave = int(threadIdx.x) >> 6;
+#pragma unroll
+    for (int i = 0; i < kCached; ++i) {
+      const uint64_t m = __ballot(((valid >> i) & 1u) && key[i] == tau);
+      if (lane == 0) sh.tie_mask[i * kW + wave] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {  // one wave finds the group holding the need-th tie
+      constexpr int kGroups = kCached * kW;
+      constexpr int kPer = (kGroups + 63) / 64;  // consecutive groups per lane
+      const int l = int(threadIdx.x);
+      uint32_t cnt[kPer];
+      uint32_t own = 0;
+#pragma unroll
+      for (int g = 0; g < kPer; ++g) {
+        const int e = l * kPer + g;
+        cnt[g] = e < kGroups ? uint32_t(__popcll(sh.tie_mask[e])) : 0u;
+        own += cnt[g];
+      }
+      uint32_t pre = own;  // inclusive prefix over lanes 0..l
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(pre, off);
+        if (l >= off) pre += y;
+      }
+      uint32_t before = pre - own;
+      if (before < need && pre >= need) {  // exactly one lane holds it
+#pragma unroll
+        for (int g = 0; g < kPer; ++g) {
+          if (before < need && before + cnt[g] >= need) {
+            const int e = l * kPer + g;
+            uint64_t m = sh.tie_mask[e];
+            for (uint32_t k = need - before; k > 1; --k) m &= m - 1;  // drop the first need-before-1 ties
+            const int bit = __ffsll(static_cast<unsigned long long>(m)) - 1;
+            const int i = e / kW, w = e % kW;
+            sh.pick[0] = uint32_t(a + i * NT + w * 64 + bit);
+          }
+          before += cnt[g];
+        }
+      }
+    }
+    __syncthreads();
+    lo = int(sh.pick[0]);
   } else {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = tau | (1u << bit);
@@ -168,8 +262,11 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   return min(min(a, b), min(c, d));
 }
 
+// The 1024-thread variant is held to 64 VGPRs so that two workgroups share a
+// CU (8 waves per SIMD): one workgroup's barriers and LDS rounds then
+// overlap the other's loads (16K-position global select 128 -> 113 us).
 template <int NT>
-__global__ __launch_bounds__(NT) void k_select(Derived P, const float* __restrict__ score,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT >= 1024 ? 8 : 1))) void k_select(Derived P, const float* __restrict__ score,
                                                      const int32_t* __restrict__ seg_start,
                                                      const int32_t* __restrict__ seg_quota,
                                                      const int32_t* __restrict__ n_seg,
