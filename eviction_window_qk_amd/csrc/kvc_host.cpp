@@ -32,7 +32,6 @@ WsLayout workspace_layout(const Derived& d) {
   L.seg_a = take(nh * S * sizeof(int32_t));
   L.seg_f = take(nh * S * sizeof(int32_t));
   L.seg_q = take(nh * S * sizeof(int32_t));
-  L.ends = take(nh * size_t(d.n_thr + 1) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -250,8 +249,7 @@ int kvc_mass_segment(const kvc_params* p, const float* u, const uint64_t* credit
       d, u, credit_in, score, d.ema ? credit_upd : nullptr, reinterpret_cast<uint64_t*>(w + L.vp),
       seg_start, seg_quota, n_seg, reinterpret_cast<uint64_t*>(w + L.seg_m),
       reinterpret_cast<int32_t*>(w + L.seg_a), reinterpret_cast<int32_t*>(w + L.seg_f),
-      reinterpret_cast<int32_t*>(w + L.seg_q), reinterpret_cast<int32_t*>(w + L.ends),
-      hipStream_t(stream)));
+      reinterpret_cast<int32_t*>(w + L.seg_q), hipStream_t(stream)));
   if (rc != KVC_OK) return rc;
   return (d.T <= d.K && !d.vlen) ? KVC_NOOP : KVC_OK;
 }
@@ -462,8 +460,7 @@ int kvc_compress_event(const kvc_params* p, const void* q_win, const void* k, co
   rc = launch_status(launch_mass_segment(
       d, u, credit_in, score, cupd, reinterpret_cast<uint64_t*>(w + L.vp), seg_start, seg_quota,
       n_seg, reinterpret_cast<uint64_t*>(w + L.seg_m), reinterpret_cast<int32_t*>(w + L.seg_a),
-      reinterpret_cast<int32_t*>(w + L.seg_f), reinterpret_cast<int32_t*>(w + L.seg_q),
-      reinterpret_cast<int32_t*>(w + L.ends), s));
+      reinterpret_cast<int32_t*>(w + L.seg_f), reinterpret_cast<int32_t*>(w + L.seg_q), s));
   if (rc != KVC_OK) return rc;
   rc = launch_status(launch_select(d, score, seg_start, seg_quota, n_seg, kept_out, s));
   if (rc != KVC_OK) return rc;

@@ -61,7 +61,7 @@ __host__ __device__ __forceinline__ Keep must_keep(int sinks, int recent, int K,
 // Workspace carve-up (byte offsets into the caller's buffer, 256-B aligned).
 struct WsLayout {
   size_t stats, u, score, cupd, vp, seg_start, seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q,
-      ends, total;
+      total;
 };
 WsLayout workspace_layout(const Derived& d);
 
@@ -72,7 +72,7 @@ hipError_t launch_mass_segment(const Derived& d, const float* u, const uint64_t*
                                float* score, uint64_t* credit_upd, uint64_t* vp,
                                int32_t* seg_start, int32_t* seg_quota, int32_t* n_seg,
                                uint64_t* seg_m, int32_t* seg_a, int32_t* seg_f, int32_t* seg_q,
-                               int32_t* ends, hipStream_t s);
+                               hipStream_t s);
 hipError_t launch_select(const Derived& d, const float* score, const int32_t* seg_start,
                          const int32_t* seg_quota, const int32_t* n_seg, int32_t* kept,
                          hipStream_t s);

@@ -53,6 +53,7 @@ struct Shared {
   int merged_a[kMaxMerged];
   int merged_b[kMaxMerged];
   int piece_off[kMaxMerged + 1];
+  int cut[kMaxMerged];  // raw cuts e_k (at most kMaxThresholds)
   int n_merged;
   union {
     float tile[NT * Tune<NT>::kSweep + 2 * kMaxHalo];  // pooling input tile with halo
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     float* __restrict__ score, uint64_t* __restrict__ credit_upd, uint64_t* __restrict__ vp,
     int32_t* __restrict__ seg_start, int32_t* __restrict__ seg_quota, int32_t* __restrict__ n_seg,
     uint64_t* __restrict__ seg_m, int32_t* __restrict__ seg_a, int32_t* __restrict__ seg_f,
-    int32_t* __restrict__ seg_q, int32_t* __restrict__ ends) {
+    int32_t* __restrict__ seg_q) {
   __shared__ Shared<NT> sh;
   constexpr int kSweep = Tune<NT>::kSweep;
   constexpr int kScanItems = Tune<NT>::kScanItems;
@@ -318,23 +319,40 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   const uint64_t* Pn = vn;
   const uint64_t V = Pn[T - 1];
 
-  // -- step 3b: thresholds theta_k = min(V, ceil(k*Delta*V)), cuts e_k
-  int32_t* en = ends + size_t(n) * (P.n_thr + 1);
+  // -- step 3b: thresholds theta_k = min(V, ceil(k*Delta*V)), cuts e_k =
+  // the first t with C(t) >= theta_k.  Each thread first loads one of NT
+  // evenly spaced samples of C into LDS; a cut is bracketed between two
+  // samples there and bisected inside the bracket, so its search takes
+  // 1 + log2(T/NT) dependent loads instead of log2(T).
+  const int stride = (T + NT - 1) / NT;
+  uint64_t* samp = sh.u.walk.m;  // 2*NT entries; the pooling tile is dead here
+  {
+    const int t = (tid + 1) * stride - 1;
+    samp[tid] = Pn[t < T - 1 ? t : T - 1];
+  }
+  __syncthreads();
   for (int kk = tid; kk < P.n_thr; kk += NT) {
     if (P.seg_fixed > 0) {  // ablation: a cut every seg_fixed positions
       const int64_t e = int64_t(kk + 1) * P.seg_fixed - 1;
-      en[kk] = e < T - 1 ? int(e) : T - 1;  // cuts past the end collapse into T-1
+      sh.cut[kk] = e < T - 1 ? int(e) : T - 1;  // cuts past the end collapse into T-1
       continue;
     }
     const double x = ceil((double(kk + 1) * P.delta) * double(V));
     uint64_t th = uint64_t(x);
     if (th > V) th = V;
-    int lo = 0, hi = T - 1;  // P[T-1] = V >= th
+    int lo = 0, hi = NT - 1;  // samp[NT-1] = C(T-1) = V >= th
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (Pn[mid] >= th) hi = mid; else lo = mid + 1;
+      if (samp[mid] >= th) hi = mid; else lo = mid + 1;
     }
-    en[kk] = lo;
+    // C(lo*stride - 1) = samp[lo-1] < th, C(min(T-1, (lo+1)*stride - 1)) >= th
+    int a = lo * stride, b = (lo + 1) * stride - 1;
+    b = b < T - 1 ? b : T - 1;
+    while (a < b) {
+      const int mid = (a + b) >> 1;
+      if (Pn[mid] >= th) b = mid; else a = mid + 1;
+    }
+    sh.cut[kk] = a;
   }
   __syncthreads();
 
@@ -343,7 +361,7 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     int nm = 0, prev_end = -1;
     int cur_a = -1, cur_b = -1;
     for (int i = 0; i <= P.n_thr; ++i) {
-      const int e = i < P.n_thr ? en[i] : T - 1;
+      const int e = i < P.n_thr ? sh.cut[i] : T - 1;
       if (e <= prev_end) continue;  // equal cuts collapse; cuts are nondecreasing
       const int a = prev_end + 1;
       prev_end = e;
@@ -571,13 +589,13 @@ hipError_t launch_mass_segment(const Derived& d, const float* u, const uint64_t*
                                float* score, uint64_t* credit_upd, uint64_t* vp,
                                int32_t* seg_start, int32_t* seg_quota, int32_t* n_seg,
                                uint64_t* seg_m, int32_t* seg_a, int32_t* seg_f, int32_t* seg_q,
-                               int32_t* ends, hipStream_t s) {
+                               hipStream_t s) {
   if (d.T >= 4096)
     k_mass_segment<1024><<<d.NH, 1024, 0, s>>>(d, u, credit_in, score, credit_upd, vp, seg_start,
-                                              seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q, ends);
+                                              seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q);
   else
     k_mass_segment<256><<<d.NH, 256, 0, s>>>(d, u, credit_in, score, credit_upd, vp, seg_start,
-                                            seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q, ends);
+                                            seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q);
   return hipGetLastError();
 }
 

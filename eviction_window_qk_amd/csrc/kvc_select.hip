@@ -95,7 +95,7 @@ __device__ uint32_t block_count(uint32_t c, Shared<NT>& sh) {
   uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) s += sh.red[i];
-  return s;
+  return __builtin_amdgcn_readfirstlane(s);
 }
 
 // The r best positions of {t in [a,b] : pred(t)} are those with key > tau,
@@ -174,8 +174,8 @@ __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint
         }
       }
       __syncthreads();
-      tau |= sh.pick[0] << shift;
-      above = sh.pick[1];
+      tau |= __builtin_amdgcn_readfirstlane(sh.pick[0]) << shift;
+      above = __builtin_amdgcn_readfirstlane(sh.pick[1]);
     }
     // xcut: the need-th tie (key == tau) in ascending position order, i.e.
     // slot-major, then thread order; ties are counted per (slot, wave).
@@ -223,7 +223,7 @@ __device__ void block_threshold(const float* __restrict__ sc, int a, int b, uint
       }
     }
     __syncthreads();
-    lo = int(sh.pick[0]);
+    lo = __builtin_amdgcn_readfirstlane(int(sh.pick[0]));
   } else {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = tau | (1u << bit);
@@ -331,12 +331,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT >= 1024 ?
     }
   }
   __syncthreads();
-  const int n_long = sh.n_long < Shared<NT>::kLongCap ? sh.n_long : Shared<NT>::kLongCap;
+  const int n_long = __builtin_amdgcn_readfirstlane(sh.n_long < Shared<NT>::kLongCap ? sh.n_long : Shared<NT>::kLongCap);
   for (int li = 0; li < n_long; ++li) {
-    const int i = sh.long_ids[li];
+    const int i = __builtin_amdgcn_readfirstlane(sh.long_ids[li]);
     int a, b;
     seg_bounds(i, &a, &b);
-    const int q = quota_of(i);
+    a = __builtin_amdgcn_readfirstlane(a);
+    b = __builtin_amdgcn_readfirstlane(b);
+    const int q = __builtin_amdgcn_readfirstlane(quota_of(i));
     uint32_t c = 0;
     for (int t = a + tid; t <= b; t += NT) c += must_keep(t) ? 0u : 1u;
     const uint32_t avail = block_count<NT>(c, sh);
