@@ -159,7 +159,9 @@ __device__ __forceinline__ bool precedes(uint64_t mx, int x, uint64_t my, int y,
   return mx < my || (mx == my && x > y);
 }
 
-template <int NT>
+// ONE: every head is one raw segment that is not split (no mass thresholds,
+// T <= seg_max or no splitting); the host decides it for the whole launch.
+template <int NT, bool ONE>
 __global__ __launch_bounds__(NT) void k_mass_segment(
     Derived P, const float* __restrict__ u, const uint64_t* __restrict__ credit_in,
     float* __restrict__ score, uint64_t* __restrict__ credit_upd, uint64_t* __restrict__ vp,
@@ -182,6 +184,14 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     score[size_t(n) * P.T + t] = 0.0f;
     if (P.ema) credit_upd[size_t(n) * P.T + t] = 0;
   }
+
+  // One raw segment (no mass thresholds) that is not split: the prefix C is
+  // then only needed for that segment's mass, C(T-1) minus the must-keep
+  // positions' share.  Both are exact sums taken during the sweeps below, so
+  // the prefix is not built, and without EMA the usage is not even stored.
+  constexpr bool one_seg = ONE;
+  const int s_end = mk.s - 1, r_beg = T - mk.r;
+  uint64_t mk_part = 0;  // usage of the must-keep positions (one_seg only)
 
   // -- step 2a/2b: pooled score and fixed-point usage w = trunc(ubar*2^40)+e,
   // one tile of NT*kSweep positions (plus the pooling halo) through LDS
@@ -211,12 +221,14 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
         sc[t] = ub;
         const float nonneg = ub > 0.0f ? ub : 0.0f;
         const uint64_t w = uint64_t(nonneg * 1099511627776.0f) + P.eps_q;  // exact 2^40 scale
-        vn[t] = w;
+        if (!one_seg || P.ema) vn[t] = w;
+        if (one_seg && (t <= s_end || t >= r_beg)) mk_part += w;
         part += w;
       }
     }
   }
   const uint64_t w_total = block_sum_u64<NT>(part, sh);
+  uint64_t v_total = w_total;  // C(T-1)
 
   // -- step 2c: EMA credit and mixed mass (Q44)
   if (P.ema) {
@@ -253,6 +265,8 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     }
     const uint64_t c_total = block_sum_u64<NT>(part, sh);
     const double cd = double(c_total);
+    part = 0;
+    mk_part = 0;
     for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
       uint64_t w[kSweep], cq[kSweep];
 #pragma unroll
@@ -268,9 +282,15 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
         const double mq = double(w[k]) / wd;
         const double nc = c_total ? double(cq[k]) / cd : 0.0;
         const double mix = (P.beta * mq) + (P.omb * nc);
-        vn[t] = uint64_t(floor(mix * 0x1p44));
+        const uint64_t v = uint64_t(floor(mix * 0x1p44));
+        vn[t] = v;
+        if (one_seg) {
+          if (t <= s_end || t >= r_beg) mk_part += v;
+          part += v;
+        }
       }
     }
+    if (one_seg) v_total = block_sum_u64<NT>(part, sh);
   }
 
   if (T <= P.K) {  // nothing to evict
@@ -281,7 +301,8 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   // -- step 2d: inclusive prefix C(t) of v, in place (the sweeps above wrote
   // v with another thread mapping)
   __syncthreads();
-  {
+  const uint64_t mk_total = one_seg ? block_sum_u64<NT>(mk_part, sh) : 0;
+  if (!one_seg) {
     uint64_t carry = 0;
     const int lane = tid & 63, wave = tid >> 6;
     for (int base = 0; base < T; base += NT * kScanItems) {
@@ -317,7 +338,7 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   }
   __syncthreads();
   const uint64_t* Pn = vn;
-  const uint64_t V = Pn[T - 1];
+  const uint64_t V = one_seg ? v_total : Pn[T - 1];
 
   // -- step 3b: thresholds theta_k = min(V, ceil(k*Delta*V)), cuts e_k =
   // the first t with C(t) >= theta_k.  Each thread first loads one of NT
@@ -326,7 +347,7 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   // 1 + log2(T/NT) dependent loads instead of log2(T).
   const int stride = (T + NT - 1) / NT;
   uint64_t* samp = sh.u.walk.m;  // 2*NT entries; the pooling tile is dead here
-  {
+  if (!one_seg) {
     const int t = (tid + 1) * stride - 1;
     samp[tid] = Pn[t < T - 1 ? t : T - 1];
   }
@@ -400,7 +421,6 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   const int ns = sh.piece_off[nm];  // <= s_cap by construction
 
   // -- step 3e: per-segment length, must-keep overlap, mass, floor
-  const int s_end = mk.s - 1, r_beg = T - mk.r;
   const size_t so = size_t(n) * P.s_cap;
   int64_t f_part = 0;
   uint64_t m_part = 0;
@@ -423,9 +443,14 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     const int end = start + len - 1;
     const int kmk = overlap_len(start, end, 0, s_end) + overlap_len(start, end, r_beg, T - 1);
     const int avail = len - kmk;
-    uint64_t mass = range_sum(Pn, start, end);
-    if (start <= s_end) mass -= range_sum(Pn, start, end < s_end ? end : s_end);
-    if (end >= r_beg) mass -= range_sum(Pn, start > r_beg ? start : r_beg, end);
+    uint64_t mass;
+    if (one_seg) {  // the segment is [0, T-1]
+      mass = V - mk_total;
+    } else {
+      mass = range_sum(Pn, start, end);
+      if (start <= s_end) mass -= range_sum(Pn, start, end < s_end ? end : s_end);
+      if (end >= r_beg) mass -= range_sum(Pn, start > r_beg ? start : r_beg, end);
+    }
     const int lmin = P.q_min < len ? P.q_min : len;
     int fl = lmin - kmk;
     fl = fl < 0 ? 0 : fl;
@@ -590,12 +615,16 @@ hipError_t launch_mass_segment(const Derived& d, const float* u, const uint64_t*
                                int32_t* seg_start, int32_t* seg_quota, int32_t* n_seg,
                                uint64_t* seg_m, int32_t* seg_a, int32_t* seg_f, int32_t* seg_q,
                                hipStream_t s) {
+  // A ragged head's real length is at most d.T, so d.T <= seg_max covers every head.
+  const bool one = d.n_thr == 0 && (d.seg_max <= 0 || d.T <= d.seg_max);
+  auto go = [&](auto kernel, int nt) {
+    kernel<<<d.NH, nt, 0, s>>>(d, u, credit_in, score, credit_upd, vp, seg_start, seg_quota, n_seg,
+                              seg_m, seg_a, seg_f, seg_q);
+  };
   if (d.T >= 4096)
-    k_mass_segment<1024><<<d.NH, 1024, 0, s>>>(d, u, credit_in, score, credit_upd, vp, seg_start,
-                                              seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q);
+    one ? go(k_mass_segment<1024, true>, 1024) : go(k_mass_segment<1024, false>, 1024);
   else
-    k_mass_segment<256><<<d.NH, 256, 0, s>>>(d, u, credit_in, score, credit_upd, vp, seg_start,
-                                            seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q);
+    one ? go(k_mass_segment<256, true>, 256) : go(k_mass_segment<256, false>, 256);
   return hipGetLastError();
 }
 

@@ -78,6 +78,14 @@ SMALL = [
     ("t1024_whole_tiles", 2, 2, 64, 128, 1024, 300, {}, 2.0),
     ("rows_120", 2, 3, 40, 128, 777, 200, {}, 1.0),
     ("t1025_chunk_edge", 2, 3, 40, 128, 1025, 200, {}, 1.0),
+    # one unsplit segment (no mass cuts): its mass is the total less the must-keep share
+    ("one_segment_must_keep", 2, 4, 32, 128, 600, 100,
+     dict(delta=1.0, seg_min=1, seg_max=0, sinks=4, recent=32), 1.0),
+    ("one_segment_within_seg_max", 2, 2, 16, 64, 400, 80, dict(delta=1.0, seg_max=512), 1.0),
+    ("one_segment_uniform", 2, 2, 16, 64, 300, 60,
+     dict(delta=1.0, seg_max=0, quota_mode=1, sinks=2, recent=8), 1.0),
+    ("one_segment_ema", 2, 2, 16, 64, 700, 150, dict(delta=1.0, seg_max=0, ema=True), 1.0),
+    ("one_segment_long", 1, 2, 16, 64, 5000, 700, dict(delta=1.0, seg_min=1, seg_max=0), 1.0),
 ]
 
 
@@ -106,6 +114,19 @@ def test_ema_credit(n_prev):
     pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K, ema=True, lam=0.9, beta=0.9)
     _run_case(pd, q, k, v, credit_in=credit if n_prev else None, n_prev=n_prev,
               label=f"ema{n_prev}")
+
+
+@pytest.mark.parametrize("T", [300, 4500])
+def test_ema_credit_one_segment(T):
+    """EMA with carried credit when the cache is one unsplit segment, for both
+    workgroup sizes of the mass/segment kernel."""
+    NH, G, W, d, K, n_prev = 2, 2, 16, 64, T // 4, 50
+    q, k, v = synth.random_small(7 + T, NH, G, W, d, T)
+    rng = np.random.default_rng(T)
+    credit = (rng.random((NH, n_prev)) * 2.0 ** 37).astype(np.uint64)
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K, ema=True, delta=1.0, seg_max=0,
+             sinks=4, recent=16)
+    _run_case(pd, q, k, v, credit_in=credit, n_prev=n_prev, label=f"ema_one_segment_{T}")
 
 
 def test_ema_credit_long_cache():

@@ -101,6 +101,8 @@ RAGGED = [
     ("multi_chunk", 3, 3, 40, 128, 1000, 200, [1000, 611, 257], {}),
     ("one_segment", 3, 4, 32, 128, 700, 100, [700, 333, 101],
      dict(delta=1.0, seg_min=1, seg_max=0, sinks=0, recent=0, pool_mode=1)),
+    ("one_segment_must_keep", 3, 2, 16, 64, 500, 100, [500, 250, 90],
+     dict(delta=1.0, seg_max=0, sinks=4, recent=16)),
     ("agg_max", 2, 4, 16, 64, 300, 60, [300, 111], dict(head_agg=1)),
     ("fixed_uniform", 3, 2, 16, 64, 640, 120, [640, 500, 129], dict(seg_fixed=48, quota_mode=1)),
 ]
