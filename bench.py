@@ -48,27 +48,29 @@ SETTLE_S = 0.25                # minimum untimed warm-up before the timed events
 
 
 def _gen_chunk(args):
-    name, heads, seed = args
+    name, heads, seed, T = args
     from eviction_window_qk_amd import synth
-    return synth.gen_heads(synth.WORKLOADS[name], heads, seed=seed)
+    return synth.gen_heads(synth.WORKLOADS[name], heads, T=T, seed=seed)
 
 
-def generate(name: str, seed=None, workers: int = 16):
-    """All heads of the workload as bf16 bits (host), in parallel chunks."""
+def generate(name: str, seed=None, workers: int = 16, T=None):
+    """All heads of the workload as bf16 bits (host), in parallel chunks
+    (T rows of K/V per head, the workload's T by default)."""
     from eviction_window_qk_amd import synth
     wl = synth.WORKLOADS[name]
     heads = list(range(wl.n_heads))
     chunks = [heads[i:i + 64] for i in range(0, len(heads), 64)]
-    G, W, d, T = wl.group, wl.window, wl.head_dim, wl.T
+    G, W, d = wl.group, wl.window, wl.head_dim
+    T = wl.T if T is None else T
     q = np.empty((wl.n_heads, G, W, d), np.uint16)
     k = np.empty((wl.n_heads, T, d), np.uint16)
     v = np.empty((wl.n_heads, T, d), np.uint16)
     if workers <= 1 or len(chunks) == 1:
-        parts = map(_gen_chunk, [(name, c, seed) for c in chunks])
+        parts = map(_gen_chunk, [(name, c, seed, T) for c in chunks])
     else:
         import multiprocessing as mp
         pool = mp.get_context("spawn").Pool(workers)
-        parts = pool.imap(_gen_chunk, [(name, c, seed) for c in chunks])
+        parts = pool.imap(_gen_chunk, [(name, c, seed, T) for c in chunks])
     for c, (qq, kk, vv) in zip(chunks, parts):
         q[c[0]:c[-1] + 1], k[c[0]:c[-1] + 1], v[c[0]:c[-1] + 1] = qq, kk, vv
     if workers > 1 and len(chunks) > 1:
@@ -277,7 +279,8 @@ def main():
         return
     cores = min(len(os.sched_getaffinity(0)), 16)
     t_gen = time.perf_counter()
-    q, k, v = generate(args.workload, workers=cores)
+    prior = bool(wl.params.get("ema")) and bool(wl.prior_seed) and not args.ragged
+    q, k, v = generate(args.workload, seed=wl.prior_seed if prior else None, workers=cores)
     print(f"[bench] generated {wl.n_heads} head-events in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
 
@@ -286,7 +289,22 @@ def main():
     dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
     del q, k, v
     ema = bool(wl.params.get("ema"))
-    n_prev = wl.budget if ema else 0
+    # A workload with a prior event times the second of two: event 0 runs here on
+    # the prior cache, event 1 on its compacted K/V plus the T - K tokens decoded
+    # since, with its credit.  Other EMA workloads start fresh (no carried credit).
+    chained = prior
+    n_prev = wl.budget if chained else 0
+    credit = None
+    if chained:
+        p0 = kvc.Params.from_dict(wl.event_params(), n_heads=wl.n_heads)
+        ev0 = kvc.compress_event(p0, dq, dk, dv)  # dq, dk, dv: the prior event's inputs
+        q1, kf, vf = generate(args.workload, workers=cores, T=wl.T - wl.budget)
+        dq = to_dev(q1)
+        dk = torch.cat([ev0["k_out"], to_dev(kf)], dim=1)
+        dv = torch.cat([ev0["v_out"], to_dev(vf)], dim=1)
+        credit = ev0["credit_out"]
+        del ev0, q1, kf, vf
+        torch.cuda.synchronize()
     variant = {}
     if args.seg_fixed:
         variant["seg_fixed"] = args.seg_fixed
@@ -297,10 +315,6 @@ def main():
     if args.ragged:
         lengths = synth.batch_valid_lengths(wl, args.ragged, seed=wl.seed)
         p.valid_len = torch.from_numpy(lengths).to(dev)
-    credit = None
-    if ema:  # carried credit from a prior event: uniform mass over the kept slots
-        credit = torch.full((wl.n_heads, n_prev), (1 << 44) // n_prev, dtype=torch.int64,
-                            device=dev)
     ws = kvc.new_workspace(p, dev)
     S = kvc.segment_capacity(p)
     u = torch.empty((wl.n_heads, wl.T), dtype=torch.float32, device=dev)
@@ -425,7 +439,8 @@ def main():
         "config": {"workload": wl.name, "n_heads": wl.n_heads, "layers": wl.layers,
                    "batch": wl.batch, "kv_heads": wl.kv_heads, "group": wl.group,
                    "head_dim": wl.head_dim, "T": wl.T, "window": wl.window,
-                   "budget": wl.budget, "ema": ema, "seed": wl.seed, **variant,
+                   "budget": wl.budget, "ema": ema, "seed": wl.seed, "n_prev": n_prev,
+                   **({"prior_event_seed": wl.prior_seed} if chained else {}), **variant,
                    **({"ragged_max_pad": args.ragged, "real_tokens": tokens} if args.ragged
                       else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
