@@ -7,7 +7,7 @@ import torch
 
 from eviction_window_qk_amd import kvc, synth
 from oracle import ams
-from parity_utils import dev_u64, host_u64
+from parity_utils import host_u64
 
 pytestmark = pytest.mark.gpu
 
