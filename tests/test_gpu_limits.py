@@ -21,6 +21,14 @@ LIMITS = [
                                                         q_min=0)),
     # about 4100 segments: past what the 1024-thread workgroup stages in LDS
     ("max_T_many_segments", 1, 1, 4, 64, 1 << 18, 8192, dict(seg_max=64)),
+    # one segment longer than select's register cache (16 keys x 1024 threads):
+    # the threshold search re-reads the scores bit by bit
+    ("segment_past_register_cache", 2, 2, 16, 64, 20000, 3000,
+     dict(delta=1.0, seg_min=1, seg_max=0)),
+    # floors of 1250 segments (q_min = 2) exceed the budget: the over-budget repair
+    # runs over a 20000-position cache, also past the register cache
+    ("repair_past_register_cache", 1, 2, 16, 64, 20000, 2000,
+     dict(seg_min=16, seg_max=16, q_min=2)),
 ]
 
 
