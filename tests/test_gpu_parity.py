@@ -205,17 +205,20 @@ def test_kept_drives_gather_of_arbitrary_indices():
             np.testing.assert_array_equal(ko[n, j], expect)
 
 
-def test_select_with_caller_quotas_under_budget():
+@pytest.mark.parametrize("T,K", [(500, 80), (8000, 700), (20000, 1500)])
+def test_select_with_caller_quotas_under_budget(T, K):
     """Caller-supplied quotas that sum below the budget: the under-budget
-    repair fills with the best unselected positions (oracle select)."""
-    NH, T, K = 2, 500, 80
-    pd = _pd(group=1, window=1, head_dim=64, T=T, budget=K, seg_max=100, seg_min=16)
+    repair fills with the best unselected positions (oracle select).  The
+    three lengths take the 256-thread workgroup, the 1024-thread one with the
+    keys in registers, and the 1024-thread one re-reading them."""
+    NH = 2
+    pd = _pd(group=1, window=1, head_dim=64, T=T, budget=K, seg_max=T // 5, seg_min=16)
     p = kvc_params(pd, NH)
     op = oracle_params(pd)
-    rng = np.random.default_rng(5)
+    rng = np.random.default_rng(5 + T)
     score = (rng.random((NH, T)) * 10).astype(np.float32)
     score[:, ::7] = score[:, :1]                           # ties
-    starts = np.array([0, 100, 200, 300, 400], np.int32)
+    starts = np.arange(0, T, T // 5, dtype=np.int32)[:5]
     S = kvc.segment_capacity(p)
     seg_start = np.zeros((NH, S), np.int32)
     seg_quota = np.zeros((NH, S), np.int32)
