@@ -22,8 +22,11 @@ Prints ONE JSON line:
   value          cached tokens scored per second (n_heads * T / step time)
   roofline       the score stage (the dominant kernels: row statistics,
                  column sums, fill) timed live with HIP events on the launch
-                 stream: algorithmic flops (one causal QK^T) / duration,
-                 against the bf16 dense MFMA peak
+                 stream: algorithmic flops (one causal QK^T) / duration against
+                 the bf16 dense MFMA peak, or, where the stage's arithmetic
+                 intensity is below the ridge (the 16K global workload),
+                 algorithmic bytes (one read of K and Q, the write of u) /
+                 duration against HBM; mfma_frac is the flop view either way
   cpu_baseline   the CPU oracle (test infrastructure, not tuned) timed on this
                  host's cores on a bounded sample of the same workload
 """
@@ -418,7 +421,18 @@ def main():
                  "frac": b_gp / (gp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     alg = algorithmic(wl, lengths)
     tokens = wl.n_heads * wl.T if lengths is None else int(lengths.sum())
+    # The score stage's bound from its own arithmetic intensity: one causal QK^T
+    # against one read of K and Q (and the write of u).  Every workload but the
+    # 16K global one (128 query rows per head) sits above the ridge.
+    score_hbm_bound = alg["b_score"] / (PEAK_HBM_GBS * 1e9) > alg["flops"] / (PEAK_BF16_TFLOPS * 1e12)
     achieved = alg["flops"] / (score_ms * 1e-3) / 1e12
+    if score_hbm_bound:
+        achieved_gbs = alg["b_score"] / (score_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / PEAK_HBM_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
     t_roof = max(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12), alg["b_total"] / (PEAK_HBM_GBS * 1e9))
     gather_gbs = alg["b_gather"] / (stage_ms[3] * 1e-3) / 1e9
     line = {
@@ -442,11 +456,12 @@ def main():
                    **({"prior_event_seed": wl.prior_seed} if chained else {}), **variant,
                    **({"ragged_max_pad": args.ragged, "real_tokens": tokens} if args.ragged
                       else {})},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+        "roofline": {**roof,
                      "traffic": None if (args.ragged or variant) else recorded_traffic(wl.name),
                      "kernel": "score stage (k_rowstats + k_colsum + k_fill)",
-                     "algorithmic_flops_per_launch": alg["flops"]},
+                     "algorithmic_flops_per_launch": alg["flops"],
+                     "algorithmic_bytes_per_launch": alg["b_score"],
+                     "mfma_frac": achieved / PEAK_BF16_TFLOPS},
         "events_per_s": 1000.0 / ms,
         "event_roofline_frac": t_roof / (ms * 1e-3),
         "score_stage_ms": score_ms,
