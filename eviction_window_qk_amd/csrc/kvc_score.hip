@@ -469,22 +469,39 @@ __global__ __launch_bounds__(kCsThreads, SUM ? 3 : 2) void k_colsum(Derived P, c
 
 // Positions T-W+1 .. T-1 are seen by fewer than W queries: replace them by
 // the maximum usage over the fully observed positions 0 .. T-W (positions of
-// the head's real tokens; the padding of a left-padded head gets 0).
-__global__ __launch_bounds__(256) void k_fill(Derived P, float* __restrict__ u) {
-  __shared__ float red[4];
+// the head's real tokens; the padding of a left-padded head gets 0).  One
+// workgroup per head; each thread keeps kLoads loads in flight per sweep
+// (clamped indices, no branches), so a long cache is not read one load at a
+// time (128K-token event: score stage 9.99 -> 9.69 ms).
+template <int NT>
+__global__ __launch_bounds__(NT) void k_fill(Derived P, float* __restrict__ u) {
+  constexpr int kLoads = 8;
+  __shared__ float red[NT / 64];
   const int n = blockIdx.x;
   const Span sp = head_span(P, n);
   const int T = sp.T, W = P.W;
-  for (int t = threadIdx.x; t < sp.off; t += 256) u[size_t(n) * P.T + t] = 0.0f;  // padding
+  for (int t = threadIdx.x; t < sp.off; t += NT) u[size_t(n) * P.T + t] = 0.0f;  // padding
   float* un = u + size_t(n) * P.T + sp.off;
+  const int last = T - W;  // fully observed: 0 .. last
   float m = -INFINITY;
-  for (int t = threadIdx.x; t <= T - W; t += 256) m = fmaxf(m, un[t]);
+  for (int t0 = threadIdx.x; t0 <= last; t0 += NT * kLoads) {
+    float x[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int t = t0 + i * NT;
+      x[i] = un[t <= last ? t : last];  // a clamped copy repeats a value already in the max
+    }
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) m = fmaxf(m, x[i]);
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  for (int t = T - W + 1 + threadIdx.x; t < T; t += 256) un[t] = m;
+  m = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) m = fmaxf(m, red[i]);
+  for (int t = last + 1 + threadIdx.x; t < T; t += NT) un[t] = m;
 }
 
 }  // namespace
@@ -508,7 +525,12 @@ hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u
     else
       k_colsum<64, false><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
   }
-  if (d.W > 1) k_fill<<<d.NH, 256, 0, s>>>(d, u);
+  if (d.W > 1) {
+    if (d.T >= 4096)
+      k_fill<1024><<<d.NH, 1024, 0, s>>>(d, u);
+    else
+      k_fill<256><<<d.NH, 256, 0, s>>>(d, u);
+  }
   return hipGetLastError();
 }
 
