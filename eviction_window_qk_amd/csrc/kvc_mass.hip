@@ -188,10 +188,18 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   // One raw segment (no mass thresholds) that is not split: the prefix C is
   // then only needed for that segment's mass, C(T-1) minus the must-keep
   // positions' share.  Both are exact sums taken during the sweeps below, so
-  // the prefix is not built, and without EMA the usage is not even stored.
+  // the prefix is not built.
   constexpr bool one_seg = ONE;
   const int s_end = mk.s - 1, r_beg = T - mk.r;
   uint64_t mk_part = 0;  // usage of the must-keep positions (one_seg only)
+
+  // The fixed-point usage is a function of the stored pooled score (the same
+  // float, so the same integer): later sweeps recompute it from the 4-byte
+  // score instead of storing and re-reading an 8-byte copy.
+  auto usage_q = [&](float ub) -> uint64_t {
+    const float nonneg = ub > 0.0f ? ub : 0.0f;
+    return uint64_t(nonneg * 1099511627776.0f) + P.eps_q;  // exact 2^40 scale
+  };
 
   // -- step 2a/2b: pooled score and fixed-point usage w = trunc(ubar*2^40)+e,
   // one tile of NT*kSweep positions (plus the pooling halo) through LDS
@@ -219,9 +227,7 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
       if (t < T) {
         const float ub = pooled(sh.u.tile, t_base, T, t, h, P.pool_mode);
         sc[t] = ub;
-        const float nonneg = ub > 0.0f ? ub : 0.0f;
-        const uint64_t w = uint64_t(nonneg * 1099511627776.0f) + P.eps_q;  // exact 2^40 scale
-        if (!one_seg || P.ema) vn[t] = w;
+        const uint64_t w = usage_q(ub);
         if (one_seg && (t <= s_end || t >= r_beg)) mk_part += w;
         part += w;
       }
@@ -230,18 +236,29 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   const uint64_t w_total = block_sum_u64<NT>(part, sh);
   uint64_t v_total = w_total;  // C(T-1)
 
-  // -- step 2c: EMA credit and mixed mass (Q44)
+  // -- step 2c: EMA credit and mixed mass (Q44).  The credit is swept here;
+  // the mixed mass v is formed where it is consumed (the prefix scan, or the
+  // one-segment sums).
+  uint64_t* cu = P.ema ? credit_upd + size_t(n) * P.T + sp.off : nullptr;
+  const double wd = double(w_total);
+  uint64_t c_total = 0;
+  double cd = 0.0;
+  auto mixed = [&](uint64_t w, uint64_t cq) -> uint64_t {
+    const double mq = double(w) / wd;
+    const double nc = c_total ? double(cq) / cd : 0.0;
+    const double mix = (P.beta * mq) + (P.omb * nc);
+    return uint64_t(floor(mix * 0x1p44));
+  };
   if (P.ema) {
-    uint64_t* cu = credit_upd + size_t(n) * P.T + sp.off;
     const uint64_t* ci = credit_in ? credit_in + size_t(n) * P.n_prev : nullptr;
-    const double wd = double(w_total);
     part = 0;
     for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
-      uint64_t w[kSweep], cin[kSweep];
+      float sv[kSweep];
+      uint64_t cin[kSweep];
 #pragma unroll
       for (int k = 0; k < kSweep; ++k) {  // loads first, clamped (no branches)
         const int t = t0 + k * NT;
-        w[k] = vn[t < T ? t : T - 1];
+        sv[k] = sc[t < T ? t : T - 1];
         cin[k] = 0;
       }
       if (P.n_prev > 0) {
@@ -255,7 +272,7 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
       for (int k = 0; k < kSweep; ++k) {
         const int t = t0 + k * NT;
         if (t >= T) continue;
-        const double mq = double(w[k]) / wd;
+        const double mq = double(usage_q(sv[k])) / wd;
         const double c = t < P.n_prev ? double(cin[k]) * 0x1p-44 : floor(mq * 0x1p44) * 0x1p-44;
         const double c_new = (P.lam * c) + (P.oml * mq);
         const uint64_t cq = uint64_t(floor(c_new * 0x1p44));
@@ -263,34 +280,31 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
         part += cq;
       }
     }
-    const uint64_t c_total = block_sum_u64<NT>(part, sh);
-    const double cd = double(c_total);
-    part = 0;
-    mk_part = 0;
-    for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
-      uint64_t w[kSweep], cq[kSweep];
+    c_total = block_sum_u64<NT>(part, sh);
+    cd = double(c_total);
+    if (one_seg) {  // the mixed masses' total and must-keep share
+      part = 0;
+      mk_part = 0;
+      for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
+        float sv[kSweep];
+        uint64_t cq[kSweep];
 #pragma unroll
-      for (int k = 0; k < kSweep; ++k) {  // clamped loads (positions past T are skipped below)
-        const int t = t0 + k * NT;
-        w[k] = vn[t < T ? t : T - 1];
-        cq[k] = cu[t < T ? t : T - 1];
-      }
+        for (int k = 0; k < kSweep; ++k) {  // clamped loads (positions past T are skipped below)
+          const int t = t0 + k * NT;
+          sv[k] = sc[t < T ? t : T - 1];
+          cq[k] = cu[t < T ? t : T - 1];
+        }
 #pragma unroll
-      for (int k = 0; k < kSweep; ++k) {
-        const int t = t0 + k * NT;
-        if (t >= T) continue;
-        const double mq = double(w[k]) / wd;
-        const double nc = c_total ? double(cq[k]) / cd : 0.0;
-        const double mix = (P.beta * mq) + (P.omb * nc);
-        const uint64_t v = uint64_t(floor(mix * 0x1p44));
-        vn[t] = v;
-        if (one_seg) {
+        for (int k = 0; k < kSweep; ++k) {
+          const int t = t0 + k * NT;
+          if (t >= T) continue;
+          const uint64_t v = mixed(usage_q(sv[k]), cq[k]);
           if (t <= s_end || t >= r_beg) mk_part += v;
           part += v;
         }
       }
+      v_total = block_sum_u64<NT>(part, sh);
     }
-    if (one_seg) v_total = block_sum_u64<NT>(part, sh);
   }
 
   if (T <= P.K) {  // nothing to evict
@@ -298,8 +312,8 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     return;
   }
 
-  // -- step 2d: inclusive prefix C(t) of v, in place (the sweeps above wrote
-  // v with another thread mapping)
+  // -- step 2d: inclusive prefix C(t) of v (usage, or the mixed mass with
+  // EMA), formed from the stored score (and credit) as the scan reads them
   __syncthreads();
   const uint64_t mk_total = one_seg ? block_sum_u64<NT>(mk_part, sh) : 0;
   if (!one_seg) {
@@ -308,10 +322,19 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     for (int base = 0; base < T; base += NT * kScanItems) {
       uint64_t x[kScanItems];
       const int i0 = base + tid * kScanItems;
+      float sv[kScanItems];
+      uint64_t cq[kScanItems];
 #pragma unroll
-      for (int i = 0; i < kScanItems; ++i) x[i] = vn[i0 + i < T ? i0 + i : T - 1];
+      for (int i = 0; i < kScanItems; ++i) {  // clamped loads, then the values
+        const int t = i0 + i < T ? i0 + i : T - 1;
+        sv[i] = sc[t];
+        cq[i] = P.ema ? cu[t] : 0;
+      }
 #pragma unroll
-      for (int i = 0; i < kScanItems; ++i) x[i] = i0 + i < T ? x[i] : 0;
+      for (int i = 0; i < kScanItems; ++i) {
+        const uint64_t w = usage_q(sv[i]);
+        x[i] = i0 + i < T ? (P.ema ? mixed(w, cq[i]) : w) : 0;
+      }
 #pragma unroll
       for (int i = 1; i < kScanItems; ++i) x[i] += x[i - 1];
       uint64_t incl = x[kScanItems - 1];
