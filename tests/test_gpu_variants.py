@@ -105,6 +105,8 @@ RAGGED = [
      dict(delta=1.0, seg_max=0, sinks=4, recent=16)),
     ("agg_max", 2, 4, 16, 64, 300, 60, [300, 111], dict(head_agg=1)),
     ("fixed_uniform", 3, 2, 16, 64, 640, 120, [640, 500, 129], dict(seg_fixed=48, quota_mode=1)),
+    # T >= 4096: the 1024-thread fill, mass/segment and select workgroups on left-padded heads
+    ("long_cache", 3, 2, 16, 64, 5000, 600, [5000, 4100, 700], {}),
 ]
 
 
