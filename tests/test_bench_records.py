@@ -34,3 +34,22 @@ def test_executed_flops_cover_two_passes():
 def test_algorithmic_flops_match_closed_form(name, flops):
     # NH * 2*d*G*(W(T-W) + W(W+1)/2) for each workload's shape
     assert bench.algorithmic(synth.WORKLOADS[name])["flops"] == pytest.approx(flops, rel=2e-3)
+
+
+@pytest.mark.parametrize("name,nbytes", [("qwen7b_t768", 0.7688e9), ("llama8b_global_t16k", 4.3956e9)])
+def test_score_stage_bytes(name, nbytes):
+    # one read of K (NH*T*d*2) and of the window queries (NH*G*W*d*2), one write of u (NH*T*4)
+    wl = synth.WORKLOADS[name]
+    expect = wl.n_heads * (2.0 * wl.T * wl.head_dim + 2.0 * wl.group * wl.window * wl.head_dim + 4.0 * wl.T)
+    assert expect == pytest.approx(nbytes, rel=1e-3)
+    assert bench.algorithmic(wl)["b_score"] == pytest.approx(expect, rel=1e-12)
+
+
+@pytest.mark.parametrize("name,bound", [("qwen7b_t768", "mfma"), ("qwen7b_t1536_ema", "mfma"),
+                                        ("llama8b_t128k", "mfma"), ("llama8b_global_t16k", "hbm")])
+def test_score_roofline_bound(name, bound):
+    # the stage's bound is the slower of its flops at the MFMA peak and its bytes at the HBM peak
+    alg = bench.algorithmic(synth.WORKLOADS[name])
+    t_flop = alg["flops"] / (bench.PEAK_BF16_TFLOPS * 1e12)
+    t_byte = alg["b_score"] / (bench.PEAK_HBM_GBS * 1e9)
+    assert ("hbm" if t_byte > t_flop else "mfma") == bound
