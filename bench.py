@@ -392,6 +392,18 @@ def main():
     torch.cuda.synchronize()
     stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])
     stage_ms = stage.mean(axis=0)
+    # D: the per-event distribution (an event recorded between consecutive
+    # events; informative only -- the headline is A's block average).
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record(stream)
+    for i in range(args.steps):
+        event()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_event = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    event_pct = {"p10": float(np.percentile(per_event, 10)), "median": float(np.median(per_event)),
+                 "p90": float(np.percentile(per_event, 90))}
 
     paged = None
     if args.paged:
@@ -444,6 +456,7 @@ def main():
         "warmup": args.warmup,
         "warmup_events": n_warm,
         "ms_per_step": ms,
+        "event_ms": event_pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
