@@ -86,6 +86,10 @@ SMALL = [
      dict(delta=1.0, seg_max=0, quota_mode=1, sinks=2, recent=8), 1.0),
     ("one_segment_ema", 2, 2, 16, 64, 700, 150, dict(delta=1.0, seg_max=0, ema=True), 1.0),
     ("one_segment_long", 1, 2, 16, 64, 5000, 700, dict(delta=1.0, seg_min=1, seg_max=0), 1.0),
+    # long caches (1024-thread fill, mass/segment and select) with the MAX head
+    # aggregation and with max-pooling
+    ("agg_max_long", 1, 4, 16, 64, 5000, 600, dict(head_agg=1), 1.5),
+    ("max_pool_long", 1, 2, 16, 64, 6000, 800, dict(pool_mode=1), 1.0),
 ]
 
 
