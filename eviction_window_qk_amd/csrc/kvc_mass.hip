@@ -508,6 +508,8 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   const size_t so = size_t(n) * P.s_cap;
   int64_t f_part = 0;
   uint64_t m_part = 0;
+  int64_t own_f = 0, own_a = 0;  // segment tid's floor, room and mass, kept for the wave quota path
+  uint64_t own_m = 0;
   for (int s = tid; s < ns; s += NT) {
     int lo = 0, hi = nm - 1;  // merged segment holding piece s
     while (lo < hi) {
@@ -546,20 +548,25 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
     seg_f[so + s] = fl;
     f_part += fl;
     m_part += mass;
+    if (s == tid) {
+      own_f = fl;
+      own_a = avail;
+      own_m = mass;
+    }
   }
   const int64_t F = block_sum_i64<NT>(f_part, sh);
   const uint64_t SM = block_sum_u64<NT>(m_part, sh);
 
   // -- step 3f/3g: quotas.  Up to 64 segments (the common case) one wave does
-  // it alone, lane s holding segment s (written by this same thread in 3e),
-  // with wave reductions instead of block-wide ones; the arithmetic is the
-  // same as the block-wide version below.
+  // it alone, lane s holding segment s (computed by this same thread in 3e
+  // and still in its registers), with wave reductions instead of block-wide
+  // ones; the arithmetic is the same as the block-wide version below.
   if (ns <= 64) {
     if (tid < 64) {
       const int s = tid;
       const bool has = s < ns;
-      const int64_t fl = has ? seg_f[so + s] : 0, av = has ? seg_a[so + s] : 0;
-      const uint64_t ms = has ? seg_m[so + s] : 0;
+      const int64_t fl = has ? own_f : 0, av = has ? own_a : 0;
+      const uint64_t ms = has ? own_m : 0;
       int64_t qv = fl;
       if (F <= mk.t_keep) {
         const int64_t t_rem = mk.t_keep - F;
