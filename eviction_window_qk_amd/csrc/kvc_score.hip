@@ -190,16 +190,22 @@ __device__ __forceinline__ void rs_block(RsCtx<D>& cx, const u32x4* __restrict__
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kRsThreads, 3) void k_rowstats(Derived P, const u32x4* __restrict__ q,
+// NW waves per workgroup: 4 (256 rows); 2 (128 rows) when a head has at most
+// 128 query rows, so that no wave idles and more workgroups -- and K tile
+// loads -- share a CU (16K-token global event with W*G = 128: 2.03 -> 1.94 ms
+// for the score stage).
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void k_rowstats(Derived P, const u32x4* __restrict__ q,
                                                             const u32x4* __restrict__ k,
                                                             float* __restrict__ rowb) {
   constexpr int kPerRow = D / 8;        // u32x4 per row
   constexpr int kStride = kPerRow + 1;  // LDS row stride (one pad piece)
-  constexpr int kLoads = kRsTile * kPerRow / kRsThreads;
+  constexpr int kThreads = 64 * NW;
+  constexpr int kRows = NW * kRsRowBlocks * 32;
+  constexpr int kLoads = kRsTile * kPerRow / kThreads;
   __shared__ u32x4 ks[2][kRsTile * kStride];
 
-  const int groups = (P.R + kRsRows - 1) / kRsRows;
+  const int groups = (P.R + kRows - 1) / kRows;
   const unsigned lb = xcd_logical_block();
   const int n = lb / groups, grp = lb % groups;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(kRsThreads, 3) void k_rowstats(Derived P, const u32
   const float c = P.c_log2;
 
   RsCtx<D> cx;
-  const int row0 = grp * kRsRows + wave * (kRsRowBlocks * 32);
+  const int row0 = grp * kRows + wave * (kRsRowBlocks * 32);
   const bool wave_active = row0 < R;  // uniform per wave
 #pragma unroll
   for (int rb = 0; rb < kRsRowBlocks; ++rb) {
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(kRsThreads, 3) void k_rowstats(Derived P, const u32
   auto fetch = [&](int kt, u32x4 (&pre)[kLoads]) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int e = threadIdx.x + i * kRsThreads;
+      const int e = threadIdx.x + i * kThreads;
       int t = kt * kRsTile + e / kPerRow;
       t = t < T ? t : T - 1;  // rows past T are masked; keep the load in bounds
       pre[i] = kn[size_t(t) * kPerRow + e % kPerRow];
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(kRsThreads, 3) void k_rowstats(Derived P, const u32
   auto stash = [&](int buf, const u32x4 (&pre)[kLoads]) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int e = threadIdx.x + i * kRsThreads;
+      const int e = threadIdx.x + i * kThreads;
       ks[buf][(e / kPerRow) * kStride + e % kPerRow] = pre[i];
     }
   };
@@ -510,16 +516,20 @@ hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u
                         hipStream_t s) {
   const u32x4* qv = static_cast<const u32x4*>(q);
   const u32x4* kv = static_cast<const u32x4*>(k);
-  const unsigned g_rs = unsigned((d.R + kRsRows - 1) / kRsRows) * unsigned(d.NH);
+  const bool small_r = d.R <= 2 * kRsRowBlocks * 32;  // two-wave pass-1 workgroups
+  const int rs_rows = small_r ? 2 * kRsRowBlocks * 32 : kRsRows;
+  const unsigned g_rs = unsigned((d.R + rs_rows - 1) / rs_rows) * unsigned(d.NH);
   const unsigned g_cs = unsigned((d.T + kCsKeys - 1) / kCsKeys) * unsigned(d.NH);
   if (d.D == 128) {
-    k_rowstats<128><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, stats);
+    if (small_r) k_rowstats<128, 2><<<g_rs, 128, 0, s>>>(d, qv, kv, stats);
+    else k_rowstats<128, kRsWaves><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, stats);
     if (d.head_agg == KVC_AGG_SUM)
       k_colsum<128, true><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
     else
       k_colsum<128, false><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
   } else {
-    k_rowstats<64><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, stats);
+    if (small_r) k_rowstats<64, 2><<<g_rs, 128, 0, s>>>(d, qv, kv, stats);
+    else k_rowstats<64, kRsWaves><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, stats);
     if (d.head_agg == KVC_AGG_SUM)
       k_colsum<64, true><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
     else
