@@ -50,3 +50,23 @@ def test_segment_counts_reach_the_limits():
     assert ams.segment_capacity(p) == 1025
     p = ams.Params(T=8192, window=16, budget=2000, delta=1.0 / 1025, seg_min=1, seg_max=0)
     assert ams.segment_capacity(p) == 1025
+
+
+RESIDENT = [
+    # (label, NH, G, W, d, T, K, sampled heads): windows of at most four padded 32-row blocks on a
+    # launch with >= 8192 column-sum chunks, so pass 2 keeps the queries in LDS and walks 4 chunks
+    # per workgroup; the first case ends in a partial chunk and a partial group of chunks
+    ("resident_G4_W32", 64, 4, 32, 64, 32768 + 100, 4000, [0, 37, 63]),
+    ("resident_G2_W64", 64, 2, 64, 128, 32768, 3000, [0, 63]),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", RESIDENT, ids=[c[0] for c in RESIDENT])
+def test_resident_column_sums(case):
+    label, NH, G, W, d, T, K, heads = case
+    chunks = (T + 255) // 256
+    assert NH * chunks >= 8192 and G * ((W + 31) // 32) <= 4
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
+    q, k, v = synth.random_small(sum(map(ord, label)), NH, G, W, d, T)
+    _run_case(pd, q, k, v, heads=heads, label=label)
