@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kCsThreads, SUM ? 3 : 2) void k_colsum(Derived P, c
 // with chunks to spare: the whole window (queries and row normalisers) stays
 // in LDS, so a workgroup walks cpw consecutive 256-key chunks of one head
 // with no barrier between them instead of re-streaming the queries for each
-// chunk (16K-token global event: score stage 1.87 -> 1.78 ms).  The row
+// chunk (16K-token global event: score stage 1.87 -> 1.76 ms).  The row
 // blocks are visited in the same order as in k_colsum, so the sums are
 // identical.
 constexpr int kResBlocks = 4;
@@ -595,7 +595,7 @@ hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u
   // Small windows (at most kResBlocks padded 32-row blocks): queries resident in LDS.
   const int cs_chunks = (d.T + kCsKeys - 1) / kCsKeys;
   const bool resident = d.G * ((d.W + 31) / 32) <= kResBlocks && int64_t(cs_chunks) * d.NH >= 8192;
-  const int cpw = 4;
+  const int cpw = 8;  // measured: 2, 4, 8, 16, 32 -> 8 fastest
   const unsigned g_res = unsigned((cs_chunks + cpw - 1) / cpw) * unsigned(d.NH);
   if (d.D == 128) {
     if (small_r) k_rowstats<128, 2><<<g_rs, 128, 0, s>>>(d, qv, kv, stats);
