@@ -88,3 +88,15 @@ def test_full_sync_round_trip():
     np.testing.assert_array_equal(kf[T0:T0 + 5], new_k)
     np.testing.assert_array_equal(vf[T0:T0 + 5], -new_k)
     np.testing.assert_array_equal(kf[:T0], kf0[:T0])
+
+
+def test_partial_append_tie_takes_first_slot():
+    # Convention (the page leaves ties open): among equal lowest scores the
+    # first slot is evicted.
+    sc = np.array([0.5, 0.2, 0.9, 0.2, 0.2], np.float32)
+    pos = np.array([10, 11, 12, 13, 14])
+    kp, vp = np.zeros((5, 2)), np.zeros((5, 2))
+    slot = refresh.partial_append(sc, pos, kp, vp, np.ones(2), -np.ones(2), 99)
+    assert slot == 1 and pos[1] == 99 and sc[1] == np.inf
+    slot = refresh.partial_append(sc, pos, kp, vp, np.ones(2), -np.ones(2), 100)
+    assert slot == 3 and list(pos) == [10, 99, 12, 100, 14]

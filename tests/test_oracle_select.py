@@ -340,3 +340,93 @@ def test_segment_capacity_bounds_every_case():
             continue
         r = ams.mass_and_segments(u, cin, p)
         assert len(r.segs) <= ams.segment_capacity(p)
+
+
+# ---------------------------------------------------------------------------
+# Cut threshold: b_k = min{t : C(t) >= k*Delta} on the normalised cumulative
+# mass C(t) = P(t)/V [AMS notes, key design 2, cut equation]
+# ---------------------------------------------------------------------------
+
+def test_cut_threshold_rounds_up_between_prefix_values():
+    # P = [2, 3, 10], Delta = 0.25: C = [0.2, 0.3, 1.0]. C(0) = 0.2 < 0.25 and
+    # C(1) = 0.3 >= 0.25, so the first cut is position 1 (a threshold taken as
+    # floor(0.25 * 10) = 2 would wrongly cut at 0); 0.5 and 0.75 are first
+    # reached at position 2.
+    P = np.array([2, 3, 10], dtype=np.uint64)
+    assert ams.thresholds(10, 0.25) == [3, 5, 8]
+    assert ams.raw_cuts(P, 0.25) == [1, 2]
+
+
+@pytest.mark.parametrize("delta", [0.25, 0.125, 0.375, 0.0625, 0.1875, 0.5])
+def test_cuts_equal_exact_rational_definition(delta):
+    # Dyadic Delta: k*Delta and (k*Delta)*V are exact in fp64, so the cuts must
+    # equal the page's real-valued definition evaluated in exact rationals.
+    from fractions import Fraction
+    rng = np.random.default_rng(int(delta * 1e4))
+    for _ in range(40):
+        T = int(rng.integers(2, 60))
+        v = rng.integers(0, 50, size=T).astype(np.uint64)
+        v[int(rng.integers(0, T))] += 1
+        P = ams.prefix(v)
+        V = int(P[-1])
+        want = set()
+        k = 1
+        while k * Fraction(delta) < 1:
+            target = k * Fraction(delta)
+            want.add(next(t for t in range(T) if Fraction(int(P[t]), V) >= target))
+            k += 1
+        want.add(T - 1)
+        assert ams.raw_cuts(P, delta) == sorted(want)
+
+
+# ---------------------------------------------------------------------------
+# Under-budget repair: when the picks and must-keep fall short of the budget,
+# the highest-scored unselected positions are added [AMS notes, key design 3,
+# last paragraph]; reachable when a caller supplies short quotas
+# ---------------------------------------------------------------------------
+
+def test_under_budget_repair_adds_highest_scores():
+    # one segment of 10, no must-keep, budget 4, caller quota 1: the pick is
+    # position 1 (0.9); the repair adds the three best of the rest (0.8, 0.7,
+    # 0.6 at 3, 5, 7), not the three worst.
+    p = ams.Params(T=10, window=1, budget=4, delta=1.0, seg_min=1, seg_max=0, sinks=0,
+                   recent=0, pool_kernel=1)
+    score = np.array([0.1, 0.9, 0.3, 0.8, 0.2, 0.7, 0.05, 0.6, 0.4, 0.5], np.float32)
+    kept = ams.select(score, [(0, 9)], [1], p)
+    assert list(kept) == [1, 3, 5, 7]
+    # with must-keep ends (sink 0, recent 9) the one free slot takes 3
+    p2 = p.with_(sinks=1, recent=1)
+    assert list(ams.select(score, [(0, 9)], [1], p2)) == [0, 1, 3, 9]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_under_budget_repair_brute_force(seed):
+    # Short caller quotas on tiny caches: the kept set must be must-keep, the
+    # per-segment picks, and then the (K - #kept) unselected non-must-keep
+    # positions with the largest score sum (ties: smallest index vector).
+    rng = np.random.default_rng(4200 + seed)
+    T = int(rng.integers(6, 13))
+    K = int(rng.integers(3, T))
+    p = ams.Params(T=T, window=1, budget=K, delta=float(rng.choice([0.2, 0.34, 0.5])),
+                   seg_min=1, seg_max=int(rng.choice([0, 3, 5])), q_min=0,
+                   sinks=int(rng.integers(0, 2)), recent=int(rng.integers(0, 3)), pool_kernel=1)
+    score = (rng.integers(0, 5, size=T) / 4).astype(np.float32)      # many ties
+    r = ams.mass_and_segments(score, None, p)
+    s, rr, t_keep = ams.must_keep(p)
+    q = np.array([int(rng.integers(0, qi + 1)) for qi in r.q])       # short quotas
+    if q.sum() >= t_keep:
+        q[:] = 0
+    mk = set(range(s)) | set(range(T - rr, T))
+    picks = set()
+    for (a, b), qi in zip(r.segs, q):
+        cand = [t for t in range(a, b + 1) if t not in mk]
+        picks |= set(sorted(cand, key=lambda t: (-score[t], t))[:qi])
+    base = mk | picks
+    free = [t for t in range(T) if t not in base]
+    best = None
+    for combo in itertools.combinations(free, K - len(base)):
+        key = (-float(np.sum(score[list(combo)].astype(np.float64))), list(combo))
+        if best is None or key < best:
+            best = key
+    want = sorted(base | set(best[1]))
+    assert list(ams.select(score, r.segs, q, p)) == want

@@ -198,3 +198,18 @@ def test_ragged_clamps_short_lengths_to_the_window():
     a = ams.steps2to5_ragged(u, z, z, None, p, 3)
     b = ams.steps2to5_ragged(u, z, z, None, p, 16)
     np.testing.assert_array_equal(a.kept, b.kept)
+
+
+def test_uniform_quota_weighs_unequal_segments_alike():
+    # Convention for "no mass-weighted quota": every segment weighs 1, not its
+    # length.  Segments of 10 and 30 positions, floors 1 each, T_rem = 4:
+    # equal weights give shares (2, 2); length weights would give (1, 3).
+    p = ams.Params(T=40, window=4, budget=6, seg_min=1, seg_max=0, sinks=0, recent=0,
+                   quota_mode=ams.QUOTA_UNIFORM)
+    segs = [(0, 9), (10, 39)]
+    v = np.arange(1, 41, dtype=np.uint64)
+    assert list(ams.quotas(segs, v, p)[0]) == [3, 3]
+    # T_rem = 5: shares 2.5 round up to 3 each (one too many); the excess comes
+    # back from the higher index first (equal weights, index desc).  Length
+    # weights would give (2, 5).
+    assert list(ams.quotas(segs, v, p.with_(budget=7))[0]) == [4, 3]
