@@ -14,9 +14,11 @@ One step = one compression event over every head-event of the workload
 select -> gather, inputs resident in HBM, outputs preallocated.  W untimed
 warm-up events run first, and at least 0.25 s of them (warmup_events in the
 output counts them), then exactly K timed events.  The default
-workload is the Qwen-7B-shaped decode event (28 layers x 16 sequences x 4 KV
-heads, G=7, d=128, T=768 = budget 256 + a 512-token interval, W=128).
-Inputs are seeded synthetic data (eviction_window_qk_amd.synth).
+workload is the largest one, the Llama-3.1-8B-shaped long-context event
+(32 layers x 8 KV heads, G=4, d=128, T=131072, W=128, budget 4096, full AMS
+segmentation with EMA credit); --workload picks another (qwen7b_t768,
+qwen7b_t1536_ema, llama8b_global_t16k, tiny).  Inputs are seeded synthetic
+data (eviction_window_qk_amd.synth).
 
 Prints ONE JSON line:
   value          cached tokens scored per second (n_heads * T / step time)
@@ -28,7 +30,10 @@ Prints ONE JSON line:
                  algorithmic bytes (one read of K and Q, the write of u) /
                  duration against HBM; mfma_frac is the flop view either way
   cpu_baseline   the CPU oracle (test infrastructure, not tuned) timed on this
-                 host's cores on a bounded sample of the same workload
+                 host's cores on a bounded sample of the same workload, plus
+                 the oracle's steps 2-5 on every head of the GPU's own usage
+                 (the bit-exact check path) and whether the GPU's kept
+                 indices equal it
 """
 from __future__ import annotations
 
@@ -146,9 +151,40 @@ def _oracle_head(args):
     return time.perf_counter() - t0
 
 
-def cpu_baseline(name: str, n_heads: int, cores: int) -> dict:
-    """The oracle, as it stands, on n_heads head-events of the workload (cycling
-    through its heads: 2 * n_heads of the workload = two whole events)."""
+# Head-events in the default CPU sample: about 10-30 s of single-core oracle
+# work per workload (the fp64 window score dominates).
+CPU_SAMPLE_HEADS = {"tiny": 64, "qwen7b_t768": 3584, "qwen7b_t1536_ema": 1024,
+                    "llama8b_global_t16k": 128, "llama8b_t128k": 16}
+
+
+def _oracle_steps2to5(args):
+    """Oracle steps 2-5 of one head on the GPU's fp32 usage; returns (seconds,
+    kept)."""
+    pd, n_prev, u_row, credit_row = args
+    from oracle import ams
+    keys = set(ams.Params.__dataclass_fields__)
+    op = ams.Params(**{k: v for k, v in pd.items() if k in keys}).with_(n_prev=n_prev)
+    k0 = np.zeros((pd["T"], 1), np.uint16)
+    t0 = time.perf_counter()
+    res = ams.steps2to5(u_row, k0, k0, credit_row, op)
+    return time.perf_counter() - t0, res.kept
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name: str, n_heads: int, cores: int, gpu_u=None, gpu_kept=None, pd=None,
+                 n_prev=0, credit=None) -> dict:
+    """The oracle, as it stands, on n_heads head-events of the workload (the
+    first n_heads, cycling if more than the workload has), and its steps 2-5 on
+    the GPU's usage of every head (when given)."""
     import multiprocessing as mp
     from eviction_window_qk_amd import synth
     wl = synth.WORKLOADS[name]
@@ -157,16 +193,30 @@ def cpu_baseline(name: str, n_heads: int, cores: int) -> dict:
     heads = [i % wl.n_heads for i in range(n_heads)]
     ctx = mp.get_context("spawn")
     with ctx.Pool(cores) as pool:
-        pool.map(_oracle_head, [(name, 0)] * cores)           # warm the workers
+        pool.map(_oracle_head, [("tiny", 0)] * cores)         # warm the workers
         t0 = time.perf_counter()
         busy = pool.map(_oracle_head, [(name, n) for n in heads])
         wall = time.perf_counter() - t0
+        s25 = None
+        if gpu_u is not None:
+            args = [(pd, n_prev, gpu_u[n], None if credit is None else credit[n])
+                    for n in range(gpu_u.shape[0])]
+            t1 = time.perf_counter()
+            res = pool.map(_oracle_steps2to5, args, chunksize=4)
+            wall25 = time.perf_counter() - t1
+            exact = all(np.array_equal(kept, gpu_kept[n]) for n, (_, kept) in enumerate(res))
+            s25 = {"heads": len(args), "wall_s": wall25, "cpu_s": sum(s for s, _ in res),
+                   "tokens_per_s": len(args) * wl.T / wall25, "kept_bit_exact": exact}
     tokens = len(heads) * wl.T
-    return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(heads)} head-events ({len(heads) / wl.n_heads:.2f} events of {name}, "
-                      f"{wl.n_heads} head-events each, T={wl.T}): full oracle event per head (fp64 "
-                      f"score + exact steps 2-5), {cores} worker processes x 1 thread; "
-                      f"{sum(busy):.1f} s of CPU work in {wall:.1f} s wall"}
+    out = {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{len(heads)} head-events ({len(heads) / wl.n_heads:.3f} events of {name}, "
+                     f"{wl.n_heads} head-events each, T={wl.T}): full oracle event per head (fp64 "
+                     f"score + exact steps 2-5), {cores} worker processes x 1 thread; "
+                     f"{sum(busy):.1f} s of CPU work in {wall:.1f} s wall",
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    if s25:
+        out["oracle_steps2to5_on_gpu_usage"] = s25
+    return out
 
 
 def refresh_pieces(wl, steps: int, warmup: int) -> dict:
@@ -227,10 +277,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen7b_t768")
+    ap.add_argument("--workload", default="llama8b_t128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
-                    help="head-events in the CPU oracle sample (default: two whole events)")
+                    help="head-events in the CPU oracle sample (default: about 10-30 s of "
+                         "single-core work for the workload)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--ragged", type=int, default=0, metavar="MAX_PAD",
@@ -491,8 +542,18 @@ def main():
     if paged:
         line["paged_gather"] = paged
     if not args.no_cpu_baseline and not (args.ragged or variant):
+        # The GPU's own usage and kept indices of one more event, for the
+        # oracle's steps 2-5 (the bit-exact check path).
+        ev_u = dict(ev_out, u=u)
+        kvc.compress_event(p, dq, dk, dv, credit, ws=ws, out=ev_u, stream=stream)
+        torch.cuda.synchronize()
+        gpu_u, gpu_kept = u.cpu().numpy(), kept.cpu().numpy()
+        cred = credit.cpu().numpy().view(np.uint64) if credit is not None else None
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_heads or 2 * wl.n_heads, cores)
+        line["cpu_baseline"] = cpu_baseline(
+            args.workload, args.cpu_heads or CPU_SAMPLE_HEADS.get(args.workload, 2 * wl.n_heads),
+            cores, gpu_u=gpu_u, gpu_kept=gpu_kept, pd=wl.event_params(**variant), n_prev=n_prev,
+            credit=cred)
     print(json.dumps(line), flush=True)
 
 

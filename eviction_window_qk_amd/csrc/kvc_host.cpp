@@ -46,6 +46,12 @@ static int count_thresholds(double delta) {
   return n;
 }
 
+// Upper bound on the sum of the pooled usage of one head-event (see derive).
+static int64_t usage_bound(int W, int G, int pool_kernel, int pool_mode) {
+  const int64_t factor = pool_mode == KVC_POOL_MAX ? pool_kernel : 2;
+  return factor * int64_t(W) * W * G;
+}
+
 static int derive(const kvc_params* p, Derived* d) {
   if (p == nullptr) return KVC_EINVAL;
   if (p->n_heads < 0) return KVC_EINVAL;
@@ -59,16 +65,21 @@ static int derive(const kvc_params* p, Derived* d) {
   if (rows > kMaxRows) return KVC_EINVAL;
   // Row slots padded per query head to whole 32-row MFMA blocks.
   if (int64_t(p->group) * ((p->window + 31) / 32) * 32 > kMaxRows) return KVC_EINVAL;
-  // Fixed-point totals stay below 2^63: sum(ubar) <= 7*W*W*G.
-  if (7 * int64_t(p->window) * p->window * p->group >= (int64_t(1) << 22)) return KVC_EINVAL;
+  // Fixed-point totals stay below 2^63: step 1's usage sums to at most W*W*G
+  // (each of the W*G softmax rows sums to 1, plus W-1 filled positions of at
+  // most W*G each), and pooling multiplies that sum by less than 2 (average:
+  // each position weighs at most (2h+1)/(h+1) over its windows) or by at most
+  // the width (max), so sum(ubar) <= pool_factor*W*W*G < 2^22.
+  if (p->pool_kernel < 1 || p->pool_kernel > 63 || (p->pool_kernel & 1) == 0) return KVC_EINVAL;
+  if (p->pool_mode != KVC_POOL_AVG && p->pool_mode != KVC_POOL_MAX) return KVC_EINVAL;
+  if (usage_bound(p->window, p->group, p->pool_kernel, p->pool_mode) >= (int64_t(1) << 22))
+    return KVC_EINVAL;
   if (p->budget < 1) return KVC_EINVAL;
   if (!(p->delta > 0.0) || !isfinite(p->delta)) return KVC_EINVAL;
   const int n_thr = count_thresholds(p->delta);
   if (n_thr < 0) return KVC_EINVAL;
   if (p->seg_min < 1 || p->seg_max < 0) return KVC_EINVAL;
   if (p->q_min < 0 || p->sinks < 0 || p->recent < 0) return KVC_EINVAL;
-  if (p->pool_kernel < 1 || p->pool_kernel > 63 || (p->pool_kernel & 1) == 0) return KVC_EINVAL;
-  if (p->pool_mode != KVC_POOL_AVG && p->pool_mode != KVC_POOL_MAX) return KVC_EINVAL;
   if (p->head_agg != KVC_AGG_SUM && p->head_agg != KVC_AGG_MAX) return KVC_EINVAL;
   if (p->ema != 0 && p->ema != 1) return KVC_EINVAL;
   if (!(p->lambda >= 0.0 && p->lambda <= 1.0)) return KVC_EINVAL;

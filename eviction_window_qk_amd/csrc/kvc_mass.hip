@@ -196,8 +196,12 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   // The fixed-point usage is a function of the stored pooled score (the same
   // float, so the same integer): later sweeps recompute it from the 4-byte
   // score instead of storing and re-reading an 8-byte copy.
+  // Usage outside the documented range (negative, NaN, or past 2^23, which
+  // step 1 never produces) is clamped first, so the conversion is always
+  // defined; clamping never changes a value in range.
   auto usage_q = [&](float ub) -> uint64_t {
-    const float nonneg = ub > 0.0f ? ub : 0.0f;
+    float nonneg = ub > 0.0f ? ub : 0.0f;  // NaN -> 0
+    nonneg = nonneg < 0x1p23f ? nonneg : 0x1p23f;
     return uint64_t(nonneg * 1099511627776.0f) + P.eps_q;  // exact 2^40 scale
   };
 

@@ -547,7 +547,8 @@ __global__ __launch_bounds__(kCsThreads, 3) void k_colsum_resident(Derived P, co
 
 // Positions T-W+1 .. T-1 are seen by fewer than W queries: replace them by
 // the maximum usage over the fully observed positions 0 .. T-W (positions of
-// the head's real tokens; the padding of a left-padded head gets 0).  One
+// the head's real tokens).  The padding of a left-padded head gets 0 here,
+// also when W = 1 and there is nothing to fill.  One
 // workgroup per head; each thread keeps kLoads loads in flight per sweep
 // (clamped indices, no branches), so a long cache is not read one load at a
 // time (128K-token event: score stage 9.99 -> 9.69 ms).
@@ -559,6 +560,7 @@ __global__ __launch_bounds__(NT) void k_fill(Derived P, float* __restrict__ u) {
   const Span sp = head_span(P, n);
   const int T = sp.T, W = P.W;
   for (int t = threadIdx.x; t < sp.off; t += NT) u[size_t(n) * P.T + t] = 0.0f;  // padding
+  if (W <= 1) return;  // every position fully observed (uniform per launch)
   float* un = u + size_t(n) * P.T + sp.off;
   const int last = T - W;  // fully observed: 0 .. last
   float m = -INFINITY;
@@ -614,7 +616,7 @@ hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u
     else
       k_colsum<64, false><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
   }
-  if (d.W > 1) {
+  if (d.W > 1 || d.vlen) {  // the fill, and the zeros on a ragged head's padding
     if (d.T >= 4096)
       k_fill<1024><<<d.NH, 1024, 0, s>>>(d, u);
     else

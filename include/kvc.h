@@ -88,8 +88,11 @@ typedef struct kvc_params {
   int32_t t_stride;    /* rows allocated per head in k/v (>= T)              */
   int32_t window;      /* W recent queries, 1..T; W*G <= 4096 and
                           G*ceil(W/32)*32 <= 4096 (32-row MFMA blocks per
-                          query head); 7*W*W*G < 2^22 keeps the fixed-point
-                          usage totals below 2^63                            */
+                          query head); F*W*W*G < 2^22 with F = 2 for
+                          average pooling and F = pool_kernel for max
+                          pooling keeps the fixed-point usage totals below
+                          2^63 (step 1's usage sums to at most W*W*G per
+                          head, and pooling multiplies that by < F)        */
   int32_t budget;      /* K positions kept per head, >= 1                    */
   int32_t seg_min;     /* shortest segment after merging (>= 1), e.g. 16     */
   int32_t seg_max;     /* longest segment after splitting, e.g. 256; 0 = none*/
@@ -157,7 +160,15 @@ int kvc_score_window(const kvc_params* p, const void* q_win, const void* k, floa
  * every position (required when ema, ignored otherwise).
  * Outputs seg_start/seg_quota/n_seg as laid out above.  Integer decisions
  * follow an exact fixed-point contract, bit-identical to a sequential
- * evaluation.  Returns KVC_NOOP (n_seg = 0) when T <= budget. */
+ * evaluation.  Returns KVC_NOOP (n_seg = 0) when T <= budget.
+ * Precondition on u (not checked: it lives on the device): finite,
+ * non-negative values whose pooled sum per head is at most F*W*W*G (the bound
+ * on `window` above) -- which every u written by kvc_score_window satisfies.
+ * Out-of-range values are clamped to [0, 2^23] (NaN to 0) before the
+ * fixed-point conversion, so any input gives a valid partition, quotas that
+ * respect the segment lengths and in-range indices; but a pooled sum past
+ * 2^23 wraps the 64-bit fixed-point totals and the cuts and quotas are then
+ * not the method's. */
 int kvc_mass_segment(const kvc_params* p, const float* u, const uint64_t* credit_in,
                      float* score, uint64_t* credit_upd, int32_t* seg_start,
                      int32_t* seg_quota, int32_t* n_seg, void* ws, size_t ws_bytes,

@@ -35,8 +35,11 @@ implementation can reproduce bit for bit:
       with no fused multiply-add and truncation toward zero when a
       non-negative float becomes an integer;
   E3  scalings by powers of two are exact;
-  E4  the fixed-point totals cannot overflow because sum(ubar) <= 7*W*W*G and
-      7*W*W*G < 2^22 is required of the parameters.
+  E4  the fixed-point totals cannot overflow: the usage sums to at most W*W*G
+      per head (W*G rows summing to 1, plus W-1 filled positions of at most
+      W*G), pooling multiplies that by less than F (F = 2 for the average,
+      the width for the max), and F*W*W*G < 2^22 is required of the
+      parameters.
 
 Where the pages leave a step open, the reading taken is stated at the step
 (each one is also listed with its reason in the design notes).  This file has

@@ -104,13 +104,23 @@ def _p(**kw):
     (dict(seg_fixed=-1), -1), (dict(T=4096, seg_fixed=2), -1),  # > 1025 fixed segments
     (dict(quota_mode=2), -1),
     (dict(window=128, group=64), -1),        # W*G > 4096
-    (dict(T=2048, window=512, group=8), -1), # W*G = 4096 but 7*W*W*G >= 2^22
+    (dict(T=2048, window=512, group=8), -1), # W*G = 4096 but 2*W*W*G >= 2^22
+    # max pooling multiplies the usage sum by its width: 63*128*128*8 >= 2^22
+    (dict(T=2048, window=128, group=8, pool_mode=1, pool_kernel=63), -1),
     (dict(n_heads=-1), -1),
 ])
 def test_invalid_params(kw, code):
     p = _p(**kw)
     assert kvc.check_params(p) == code
     assert kvc.workspace_bytes(p) == 0
+
+
+def test_usage_bound_depends_on_the_pooling():
+    # the same shape passes with average pooling (2*W*W*G < 2^22) and with
+    # max pooling of width 7, but not of width 63
+    assert kvc.check_params(_p(T=2048, window=128, group=8)) == 0
+    assert kvc.check_params(_p(T=2048, window=128, group=8, pool_mode=1, pool_kernel=7)) == 0
+    assert kvc.check_params(_p(T=2048, window=128, group=8, pool_mode=1, pool_kernel=63)) == -1
 
 
 def test_valid_params_for_every_workload():

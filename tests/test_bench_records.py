@@ -12,9 +12,18 @@ import bench  # noqa: E402
 from eviction_window_qk_amd import synth  # noqa: E402
 
 
+HEADLINE = "llama8b_t128k"   # bench.py's default workload
+
+
+def test_bench_default_is_the_largest_workload():
+    wl = synth.WORKLOADS[HEADLINE]
+    assert all(wl.n_heads * wl.T >= w.n_heads * w.T for w in synth.WORKLOADS.values())
+    assert "--workload\", default=\"llama8b_t128k\"" in open(bench.__file__).read()
+
+
 def test_headline_records_are_current():
-    tr = bench.recorded_traffic("qwen7b_t768")
-    mf = bench.recorded_mfma("qwen7b_t768")
+    tr = bench.recorded_traffic(HEADLINE)
+    mf = bench.recorded_mfma(HEADLINE)
     assert tr is not None and tr > 0
     assert mf is not None
     assert set(mf["mfma_busy"]) == {"k_rowstats", "k_colsum"}
@@ -22,8 +31,8 @@ def test_headline_records_are_current():
 
 
 def test_executed_flops_cover_two_passes():
-    alg = bench.algorithmic(synth.WORKLOADS["qwen7b_t768"])
-    mf = bench.recorded_mfma("qwen7b_t768")
+    alg = bench.algorithmic(synth.WORKLOADS[HEADLINE])
+    mf = bench.recorded_mfma(HEADLINE)
     # each pass runs the causal QK^T once, diagonal 32x32 blocks whole
     assert 2 * alg["flops"] <= mf["executed_flops_per_launch"] <= 2.1 * alg["flops"]
 

@@ -1,11 +1,15 @@
 """Full-size events of every workload, in the launch configuration bench.py
 times: one kvc_compress_event over all head-events of the workload.
 
-Sampled head-events are checked against the oracle (window score to 2e-3
-relative; steps 2-5 bit for bit on the oracle's fp32 usage, fed through the
-stage entry points at full size); every head-event is checked by properties
-(valid kept lists, K/V rows equal to the gathered input rows); the event equals
-the stage entry points run in sequence, bit for bit.
+Every head-event's steps 2-5 are checked against the oracle run on the GPU's
+own fp32 usage of that event (CPU worker processes): pooled score, credit,
+segment starts, quotas, kept indices and carried credit bit for bit, and the
+compacted K/V rows equal to K[kept], V[kept] (so, with kept equal to the
+oracle's, to the oracle's gather).  The window score is compared with the fp64
+oracle on every head of the Qwen-7B and 16K global workloads and on sampled
+heads of the others (2e-3 relative); sampled heads also run the stage entry
+points on the oracle's own usage, bit for bit.  The event equals the stage
+entry points run in sequence, bit for bit.
 """
 import numpy as np
 import pytest
@@ -13,10 +17,70 @@ import torch
 
 from eviction_window_qk_amd import kvc, synth
 from oracle import ams
+import oracle_workers
 from parity_utils import (assert_usage_close, check_kept_valid, dev_bf16, dev_u64, gen_all,
                           host_bits, host_u64, kvc_params, oracle_params, widen)
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cpu_pool():
+    pool = oracle_workers.pool()
+    yield pool
+    pool.close()
+    pool.join()
+
+
+def _every_head_steps2to5(label, pd, p, u_dev: torch.Tensor, kept_dev: torch.Tensor, credit_in,
+                          credit_out_dev, n_prev, pool, lengths=None):
+    """Steps 2-5 of every head-event against the oracle fed the GPU's own usage
+    u_dev: kvc_mass_segment on u_dev gives the per-head score, credit and
+    segment tables (the event computes them identically: the event/stage
+    equality is checked separately); kept and the carried credit are the
+    event's own outputs."""
+    NH, T = u_dev.shape
+    dci = dev_u64(credit_in) if (credit_in is not None and n_prev > 0) else None
+    ws = kvc.new_workspace(p, u_dev.device)
+    ms = kvc.mass_segment(p, u_dev, dci, ws=ws)
+    torch.cuda.synchronize()
+    u = u_dev.cpu().numpy()
+    score = ms["score"].cpu().numpy().view(np.uint32)
+    n_seg, starts, quotas = (ms["n_seg"].cpu().numpy(), ms["seg_start"].cpu().numpy(),
+                             ms["seg_quota"].cpu().numpy())
+    cupd = host_u64(ms["credit_upd"]) if p.ema else None
+    kept = kept_dev.cpu().numpy()
+    cout = host_u64(credit_out_dev) if p.ema else None
+    args = [(pd, n_prev, u[n], None if dci is None else credit_in[n],
+             None if lengths is None else int(lengths[n])) for n in range(NH)]
+    print(f"[full] {label}: oracle steps 2-5 on the GPU's usage, all {NH} heads", flush=True)
+    for n, ref in enumerate(pool.imap(oracle_workers.steps2to5_head, args, chunksize=4)):
+        tag = f"{label} head {n}"
+        np.testing.assert_array_equal(score[n], ref["score"], err_msg=f"{tag}: pooled score")
+        if p.ema:
+            np.testing.assert_array_equal(cupd[n], ref["credit_upd"], err_msg=f"{tag}: credit")
+            np.testing.assert_array_equal(cout[n], ref["credit_out"], err_msg=f"{tag}: credit_out")
+        if ref["noop"]:
+            assert n_seg[n] == 0, tag
+        else:
+            ns = len(ref["starts"])
+            assert n_seg[n] == ns, f"{tag}: {n_seg[n]} segments, oracle {ns}"
+            np.testing.assert_array_equal(starts[n, :ns], ref["starts"], err_msg=f"{tag}: starts")
+            np.testing.assert_array_equal(quotas[n, :ns], ref["quotas"], err_msg=f"{tag}: quotas")
+        np.testing.assert_array_equal(kept[n], ref["kept"], err_msg=f"{tag}: kept")
+        if (n + 1) % max(1, NH // 4) == 0:
+            print(f"[full] {label}: {n + 1}/{NH} heads bit-exact", flush=True)
+
+
+def _every_head_usage(label, name, u_gpu: np.ndarray, pool, over=None):
+    """The window score of every head-event against the fp64 oracle (inputs
+    regenerated per head in the workers)."""
+    NH = u_gpu.shape[0]
+    print(f"[full] {label}: fp64 oracle usage, all {NH} heads", flush=True)
+    args = [(name, n, over or {}) for n in range(NH)]
+    for n, u_ref in enumerate(pool.imap(oracle_workers.usage_head, args, chunksize=4)):
+        assert_usage_close(u_gpu[n], u_ref, f"{label} head {n}")
+    print(f"[full] {label}: usage within tolerance on every head", flush=True)
 
 
 def _steps2to5_sampled(pd, p, u_full: torch.Tensor, u_ref32: dict, credit_in, k_bits, v_bits,
@@ -51,7 +115,7 @@ def _steps2to5_sampled(pd, p, u_full: torch.Tensor, u_ref32: dict, credit_in, k_
     return ms
 
 
-def _check_event(name, pd, q, k, v, credit_in, n_prev, heads, label):
+def _check_event(name, pd, q, k, v, credit_in, n_prev, heads, label, pool, usage_all=False):
     NH = q.shape[0]
     T = pd["T"]
     print(f"[full] {label}: NH={NH} T={T} K={pd['budget']} sampled heads {heads}", flush=True)
@@ -88,33 +152,44 @@ def _check_event(name, pd, q, k, v, credit_in, n_prev, heads, label):
         print(f"[full] {label}: head {n} usage within tolerance", flush=True)
     _steps2to5_sampled(pd, p, ev["u"], u_ref32, credit_in, k, v, dk, dv, n_prev, heads)
     print(f"[full] {label}: steps 2-5 bit-exact on sampled heads", flush=True)
+    if usage_all:
+        _every_head_usage(label, name, u_gpu, pool, _overrides(name, pd))
+    _every_head_steps2to5(label, pd, p, ev["u"], ev["kept"], credit_in, ev.get("credit_out"),
+                          n_prev, pool)
     return ev
 
 
-def test_full_tiny():
+def _overrides(name, pd):
+    """Event parameters of pd that differ from the workload's own."""
+    base = synth.WORKLOADS[name].event_params()
+    return {k: v for k, v in pd.items() if base.get(k) != v}
+
+
+def test_full_tiny(cpu_pool):
     q, k, v = synth.gen_heads(synth.WORKLOADS["tiny"], [0])
-    _check_event("tiny", synth.WORKLOADS["tiny"].event_params(), q, k, v, None, 0, [0], "tiny")
+    _check_event("tiny", synth.WORKLOADS["tiny"].event_params(), q, k, v, None, 0, [0], "tiny",
+                 cpu_pool, usage_all=True)
 
 
-def test_full_qwen7b_t768():
+def test_full_qwen7b_t768(cpu_pool):
     name = "qwen7b_t768"
     q, k, v = gen_all(name)
     _check_event(name, synth.WORKLOADS[name].event_params(), q, k, v, None, 0,
-                 [0, 613, 1234, 1791], name)
+                 [0, 613, 1234, 1791], name, cpu_pool, usage_all=True)
 
 
-def test_full_qwen7b_t1536_ema_chain():
+def test_full_qwen7b_t1536_ema_chain(cpu_pool):
     """Event 0 on the fresh cache, then event 1 on the compacted cache plus the
     512 tokens since, with the carried credit.  Sampled heads take their event-1
-    inputs from the oracle's event 0; the other heads from the GPU's (they are
-    checked by properties only)."""
+    inputs from the oracle's event 0; the other heads from the GPU's."""
     name = "qwen7b_t1536_ema"
     wl = synth.WORKLOADS[name]
     pd = wl.event_params()
     K, T = wl.budget, wl.T
     heads = [0, 3333, 7167]
     q0, k0, v0 = gen_all(name, seed=wl.prior_seed)
-    ev0 = _check_event(name, pd, q0, k0, v0, None, 0, heads[:1], "qwen7b_t1536_ema event 0")
+    ev0 = _check_event(name, pd, q0, k0, v0, None, 0, heads[:1], "qwen7b_t1536_ema event 0",
+                       cpu_pool)
     k_out = host_bits(ev0["k_out"])
     v_out = host_bits(ev0["v_out"])
     credit = host_u64(ev0["credit_out"])
@@ -128,32 +203,40 @@ def test_full_qwen7b_t1536_ema_chain():
     q1, kf, vf = gen_all(name, T=T - K)           # fresh queries and the new tokens
     k1 = np.concatenate([k_out, kf], axis=1)
     v1 = np.concatenate([v_out, vf], axis=1)
-    _check_event(name, pd, q1, k1, v1, credit, K, heads, "qwen7b_t1536_ema event 1")
+    _check_event(name, pd, q1, k1, v1, credit, K, heads, "qwen7b_t1536_ema event 1", cpu_pool)
 
 
-def test_full_llama8b_global_t16k():
+def test_full_llama8b_global_t16k(cpu_pool):
+    """The one-segment global top-2048 at full size: the headline SUM over the
+    four query heads, then the same inputs with the MAX head aggregation."""
     name = "llama8b_global_t16k"
     q, k, v = gen_all(name)
-    _check_event(name, synth.WORKLOADS[name].event_params(), q, k, v, None, 0, [0, 1023], name)
+    pd = synth.WORKLOADS[name].event_params()
+    _check_event(name, pd, q, k, v, None, 0, [0, 1023], name, cpu_pool, usage_all=True)
+    pd_max = synth.WORKLOADS[name].event_params(head_agg=ams.AGG_MAX)
+    _check_event(name, pd_max, q, k, v, None, 0, [0, 511, 1023], f"{name} head_agg=max", cpu_pool,
+                 usage_all=True)
 
 
-def test_full_llama8b_t128k():
+def test_full_llama8b_t128k(cpu_pool):
     name = "llama8b_t128k"
     q, k, v = gen_all(name, chunk=4)
-    ev = _check_event(name, synth.WORKLOADS[name].event_params(), q, k, v, None, 0, [0, 200], name)
+    ev = _check_event(name, synth.WORKLOADS[name].event_params(), q, k, v, None, 0, [0, 200], name,
+                      cpu_pool)
     assert int(ev["kept"].shape[1]) == 4096
 
 
-def test_full_qwen7b_t768_fixed_uniform():
+def test_full_qwen7b_t768_fixed_uniform(cpu_pool):
     """The two quota/segment ablations together at full size (the bench's
     --seg-fixed 64 --quota-mode uniform run)."""
     name = "qwen7b_t768"
     q, k, v = gen_all(name)
     pd = synth.WORKLOADS[name].event_params(seg_fixed=64, quota_mode=ams.QUOTA_UNIFORM)
-    _check_event(name, pd, q, k, v, None, 0, [0, 999, 1791], "qwen7b_t768 fixed64+uniform")
+    _check_event(name, pd, q, k, v, None, 0, [0, 999, 1791], "qwen7b_t768 fixed64+uniform",
+                 cpu_pool)
 
 
-def test_full_qwen7b_t768_ragged():
+def test_full_qwen7b_t768_ragged(cpu_pool):
     """A left-padded batch at full size (the bench's --ragged 400 run): each
     batch element's prompt is shorter by 0..400 tokens."""
     name = "qwen7b_t768"
@@ -207,3 +290,5 @@ def test_full_qwen7b_t768_ragged():
         np.testing.assert_array_equal(host_bits(ko[n]), res.k_out, err_msg=f"head {n} K_out")
         np.testing.assert_array_equal(host_bits(vo[n]), res.v_out, err_msg=f"head {n} V_out")
     print(f"[full] ragged {name}: sampled heads bit-exact", flush=True)
+    _every_head_steps2to5(f"ragged {name}", pd, p, ev["u"], ev["kept"], None, None, 0, cpu_pool,
+                          lengths=lengths)

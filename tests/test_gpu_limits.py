@@ -54,7 +54,7 @@ def test_segment_counts_reach_the_limits():
 
 RESIDENT = [
     # (label, NH, G, W, d, T, K, sampled heads): windows of at most four padded 32-row blocks on a
-    # launch with >= 8192 column-sum chunks, so pass 2 keeps the queries in LDS and walks 4 chunks
+    # launch with >= 8192 column-sum chunks, so pass 2 keeps the queries in LDS and walks 8 chunks
     # per workgroup; the first case ends in a partial chunk and a partial group of chunks
     ("resident_G4_W32", 64, 4, 32, 64, 32768 + 100, 4000, [0, 37, 63]),
     ("resident_G2_W64", 64, 2, 64, 128, 32768, 3000, [0, 63]),
@@ -70,3 +70,59 @@ def test_resident_column_sums(case):
     pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
     q, k, v = synth.random_small(sum(map(ord, label)), NH, G, W, d, T)
     _run_case(pd, q, k, v, heads=heads, label=label)
+
+
+@pytest.mark.gpu
+def test_resident_and_streamed_column_sums_agree_bitwise():
+    """Pass 2 takes the LDS-resident kernel on a launch with >= 8192 column-sum
+    chunks and the streamed one otherwise; both visit the row blocks in the same
+    order, so a head's usage has the same bits whichever kernel ran it.  The
+    same heads run once inside a 64-head launch (resident) and once alone
+    (streamed)."""
+    import numpy as np
+    import torch
+    from parity_utils import dev_bf16, kvc_params
+    NH, G, W, d, T, K = 64, 4, 32, 128, 32768, 2000
+    assert NH * ((T + 255) // 256) >= 8192 and 4 * ((T + 255) // 256) < 8192
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
+    q, k, _ = synth.random_small(31337, NH, G, W, d, T)
+    dq, dk = dev_bf16(q), dev_bf16(k)
+    u_all = kvc.score_window(kvc_params(pd, NH), dq, dk)
+    for sub in ([0, 1, 2, 3], [40, 63]):
+        idx = torch.tensor(sub, device="cuda")
+        u_sub = kvc.score_window(kvc_params(pd, len(sub)), dq[idx].contiguous(),
+                                 dk[idx].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(u_sub.view(torch.int32), u_all[idx].view(torch.int32)), sub
+    print("[case] resident vs streamed column sums: identical bits", flush=True)
+
+
+@pytest.mark.gpu
+def test_resident_column_sums_ragged():
+    """A left-padded batch on the LDS-resident pass 2 (its chunk walk stops at
+    each head's real length); sampled heads against the oracle."""
+    import numpy as np
+    import torch
+    from oracle import ams
+    from parity_utils import (assert_usage_close, check_steps2to5_ragged, dev_bf16, kvc_params,
+                              oracle_params, widen)
+    NH, G, W, d, T, K = 64, 4, 32, 64, 32768 + 100, 3000
+    assert NH * ((T + 255) // 256) >= 8192
+    rng = np.random.default_rng(77)
+    lengths = rng.integers(W, T + 1, size=NH).astype(np.int32)
+    lengths[:4] = [T, 300, W, 16000 + 37]
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
+    q, k, v = synth.random_small(2718, NH, G, W, d, T)
+    p = kvc_params(pd, NH)
+    p.valid_len = torch.from_numpy(lengths).cuda()
+    u = torch.full((NH, T), float("nan"), dtype=torch.float32, device="cuda")
+    kvc.score_window(p, dev_bf16(q), dev_bf16(k), u=u)
+    u_gpu = u.cpu().numpy()
+    op = oracle_params(pd)
+    heads = [0, 1, 2, 3, 50]
+    for n in heads:
+        u_ref = ams.window_usage_ragged(widen(q[n]), widen(k[n, :T]), op, int(lengths[n]))
+        assert_usage_close(u_gpu[n], u_ref, f"resident ragged head {n} (len {lengths[n]})")
+    assert not np.isnan(u_gpu).any()
+    check_steps2to5_ragged(pd, u_gpu, k, v, None, heads, lengths)
+    print("[case] resident ragged: sampled heads ok", flush=True)

@@ -135,3 +135,25 @@ def test_ragged_qwen7b_shape_heads():
     q, k, v = synth.gen_heads(wl, heads)
     lengths = synth.batch_valid_lengths(wl, 400, seed=1, heads=heads)
     _run_ragged(wl.event_params(), q, k, v, lengths, "ragged qwen7b_t768 sampled")
+
+
+def test_ragged_window_one_zeroes_the_padding():
+    """W = 1 has no positions to fill, but a left-padded head's usage must still
+    be 0 on its padding: the output buffer starts as NaN so that any position
+    the kernels leave unwritten fails the comparison."""
+    NH, G, W, d, T, K = 3, 4, 1, 64, 300, 40
+    lengths = np.array([T, T // 2, 5], np.int32)
+    q, k, v = synth.random_small(4242, NH, G, W, d, T)
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
+    p = kvc_params(pd, NH)
+    p.valid_len = torch.from_numpy(lengths).cuda()
+    op = oracle_params(pd)
+    dq, dk = dev_bf16(q), dev_bf16(k)
+    u = torch.full((NH, T), float("nan"), dtype=torch.float32, device="cuda")
+    kvc.score_window(p, dq, dk, u=u)
+    u_gpu = u.cpu().numpy()
+    for n in range(NH):
+        u_ref = ams.window_usage_ragged(widen(q[n]), widen(k[n, :T]), op, int(lengths[n]))
+        assert_usage_close(u_gpu[n], u_ref, f"W=1 ragged head {n}")
+        assert np.all(u_gpu[n, :T - max(int(lengths[n]), W)] == 0.0)
+    _run_ragged(pd, q, k, v, lengths, "ragged_window_one")

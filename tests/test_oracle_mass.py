@@ -175,8 +175,33 @@ def test_mass_loops_agree(ema):
 
 
 def test_overflow_bound_for_largest_workload():
-    # E4: sum(ubar) <= 7*W^2*G and 7*W^2*G*2^40 + T*e < 2^63 for every workload
-    for W, G, T in [(32, 1, 1024), (128, 7, 768), (128, 7, 1536), (32, 4, 16384), (128, 4, 131072)]:
-        assert 7 * W * W * G < 2 ** 22
-        assert 7 * W * W * G * 2 ** 40 + T * ams.eps_fixed(1e-6) < 2 ** 63
+    # E4: sum(ubar) <= F*W^2*G (F = 2 average, the width for max pooling) and
+    # F*W^2*G*2^40 + T*e < 2^63 for every workload
+    for W, G, T, F in [(32, 1, 1024, 2), (128, 7, 768, 2), (128, 7, 1536, 2), (32, 4, 16384, 7),
+                       (128, 4, 131072, 2)]:
+        assert F * W * W * G < 2 ** 22
+        assert F * W * W * G * 2 ** 40 + T * ams.eps_fixed(1e-6) < 2 ** 63
     assert math.ceil(1e-6 * 2 ** 40) == 1099512
+
+
+@pytest.mark.parametrize("mode,width", [(ams.POOL_AVG, 7), (ams.POOL_AVG, 1), (ams.POOL_AVG, 63),
+                                        (ams.POOL_MAX, 7), (ams.POOL_MAX, 63)])
+def test_pooled_usage_sum_bound(mode, width):
+    # The bound the parameters are checked against: the filled usage sums to
+    # at most W*W*G, and pooling multiplies that by less than 2 (average) or by
+    # at most the width (max).  The extreme case is every query attending to
+    # one key (its usage W*G, copied by the fill into W-1 positions).
+    rng = np.random.default_rng(width)
+    W, G, T, d = 8, 3, 200, 16
+    F = width if mode == ams.POOL_MAX else 2
+    p = ams.Params(T=T, window=W, budget=16, group=G, head_dim=d, pool_kernel=width,
+                   pool_mode=mode)
+    for trial in range(4):
+        k = rng.standard_normal((T, d))
+        q = rng.standard_normal((G, W, d))
+        if trial >= 2:                     # one key dominates every row
+            k[int(rng.integers(0, T - W))] = 40.0 * np.sign(q.sum(axis=(0, 1)))
+        u = ams.window_usage(q, k, p)
+        assert u.sum() <= W * W * G * (1 + 1e-12)
+        assert float(ams.pool(u.astype(np.float32), p).astype(np.float64).sum()) <= \
+            F * W * W * G * (1 + 1e-6)
