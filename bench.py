@@ -154,7 +154,7 @@ def _oracle_head(args):
 # Head-events in the default CPU sample: about 10-30 s of single-core oracle
 # work per workload (the fp64 window score dominates).
 CPU_SAMPLE_HEADS = {"tiny": 64, "qwen7b_t768": 3584, "qwen7b_t1536_ema": 1024,
-                    "llama8b_global_t16k": 128, "llama8b_t128k": 16}
+                    "llama8b_global_t16k": 128, "llama8b_t128k": 32}
 
 
 def _oracle_steps2to5(args):
