@@ -35,10 +35,12 @@ SOURCES = {
     "kvc_select.hip": [],
     "kvc_gather.hip": [],
     "kvc_refresh.hip": ["-ffp-contract=off"],  # fp64 cosine: one operation at a time
+    "kvc_noalloc.hip": [],
 }
 EXPORTS = ["kvc_score_window", "kvc_mass_segment", "kvc_select", "kvc_gather_compact",
            "kvc_gather_paged", "kvc_qc_trigger", "kvc_partial_init", "kvc_partial_append",
-           "kvc_full_sync", "kvc_compress_event", "kvc_workspace_bytes", "kvc_segment_capacity",
+           "kvc_full_sync", "kvc_compress_event", "kvc_compress_event_noalloc",
+           "kvc_workspace_bytes", "kvc_segment_capacity",
            "kvc_check_params", "kvc_strerror", "kvc_abi_version"]
 
 

@@ -188,6 +188,7 @@ const char* kvc_strerror(int status) {
     case KVC_EWORKSPACE: return "workspace missing or smaller than kvc_workspace_bytes()";
     case KVC_EUNSUPPORTED: return "unsupported variant: head_dim must be 64 or 128 and group <= 64";
     case KVC_EDEVICE: return "HIP runtime reported a launch error";
+    case KVC_ESCRATCH: return "event needs more scratch than kvc_compress_event_noalloc holds (KVC_NOALLOC_SCRATCH_BYTES); use kvc_compress_event with a workspace";
     default: return "unknown status";
   }
 }

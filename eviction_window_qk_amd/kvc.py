@@ -23,6 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
 OK, NOOP = 0, 1
+ESCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KVC_NOALLOC_SCRATCH_BYTES
 POOL_AVG, POOL_MAX = 0, 1
 AGG_SUM, AGG_MAX = 0, 1
 QUOTA_MASS, QUOTA_UNIFORM = 0, 1
@@ -110,7 +112,7 @@ class Params:
 
 # The kvc_params layout and entry-point signatures this binding marshals
 # (KVC_ABI_VERSION in include/kvc.h); a library of another version is refused.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 
@@ -134,6 +136,7 @@ def lib() -> ctypes.CDLL:
         "kvc_gather_paged": [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, vp, vp, vp, vp,
                              ctypes.c_int32, vp, ctypes.c_int32, vp, vp, vp, vp, vp],
         "kvc_compress_event": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "kvc_compress_event_noalloc": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "kvc_qc_trigger": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
                            ctypes.c_double, ctypes.c_int32, vp, vp, vp],
         "kvc_partial_init": [P, vp, vp, vp, vp, vp],
@@ -390,6 +393,35 @@ def compress_event(p: Params, q, k, v, credit_in=None, ws=None, out=None, want_u
         _ptr(o.get("u"), (torch.float32,), (p.n_heads, p.T), "u_out"), ws.data_ptr(),
         ws.numel(), _stream(stream))
     o["status"] = _check(rc, "kvc_compress_event")
+    return o
+
+
+def compress_event_noalloc(p: Params, q, k, v, credit_in=None, out=None, want_u=False,
+                           stream=None):
+    """The whole event through kvc_compress_event_noalloc (library-held scratch,
+    no workspace).  Returns dict(k_out, v_out, credit_out, kept, u, status)."""
+    dev = _device(q, k, v)
+    shp = (p.n_heads, p.budget, p.head_dim)
+    o = dict(out or {})
+    o.setdefault("k_out", torch.empty(shp, dtype=k.dtype, device=dev))
+    o.setdefault("v_out", torch.empty(shp, dtype=v.dtype, device=dev))
+    o.setdefault("kept", torch.empty((p.n_heads, p.budget), dtype=torch.int32, device=dev))
+    if p.ema:
+        o.setdefault("credit_out", torch.empty((p.n_heads, p.budget), dtype=torch.int64, device=dev))
+    if want_u:
+        o.setdefault("u", torch.empty((p.n_heads, p.T), dtype=torch.float32, device=dev))
+    c = p.to_c()
+    rc = lib().kvc_compress_event_noalloc(
+        ctypes.byref(c),
+        _ptr(q, _BF16_LIKE, (p.n_heads, p.group, p.window, p.head_dim), "q_win"),
+        _ptr(k, _BF16_LIKE, (p.n_heads, p.stride, p.head_dim), "k"),
+        _ptr(v, _BF16_LIKE, (p.n_heads, p.stride, p.head_dim), "v"),
+        _ptr(credit_in, (torch.int64,), (p.n_heads, p.n_prev), "credit_in"),
+        _ptr(o["k_out"], _BF16_LIKE, shp, "k_out"), _ptr(o["v_out"], _BF16_LIKE, shp, "v_out"),
+        _ptr(o.get("credit_out"), (torch.int64,), (p.n_heads, p.budget), "credit_out"),
+        _ptr(o["kept"], (torch.int32,), (p.n_heads, p.budget), "kept"),
+        _ptr(o.get("u"), (torch.float32,), (p.n_heads, p.T), "u_out"), _stream(stream))
+    o["status"] = _check(rc, "kvc_compress_event_noalloc")
     return o
 
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 enum kvc_status {
   KVC_OK = 0,
@@ -70,8 +70,13 @@ enum kvc_status {
   KVC_EALIGN = -2,        /* a pointer is not aligned as required           */
   KVC_EWORKSPACE = -3,    /* ws is NULL or ws_bytes < kvc_workspace_bytes() */
   KVC_EUNSUPPORTED = -4,  /* head_dim or group outside the built variants   */
-  KVC_EDEVICE = -5        /* the HIP runtime reported a launch error        */
+  KVC_EDEVICE = -5,       /* the HIP runtime reported a launch error        */
+  KVC_ESCRATCH = -6       /* kvc_compress_event_noalloc: the event needs more
+                             scratch than KVC_NOALLOC_SCRATCH_BYTES          */
 };
+
+/* Scratch held on each GPU by kvc_compress_event_noalloc (64 MiB). */
+#define KVC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 enum { KVC_POOL_AVG = 0, KVC_POOL_MAX = 1 };
 enum { KVC_AGG_SUM = 0, KVC_AGG_MAX = 1 };
@@ -280,6 +285,26 @@ int kvc_compress_event(const kvc_params* p, const void* q_win, const void* k, co
                        const uint64_t* credit_in, void* k_out, void* v_out,
                        uint64_t* credit_out, int32_t* kept_out, float* u_out, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* The whole event exactly as kvc_compress_event (same arguments, same
+ * results, bit for bit), for callers that cannot allocate device memory:
+ * code under HIP graph capture, serving loops and harnesses that forbid
+ * allocation.  Instead of a workspace argument it uses scratch memory the
+ * library holds on each GPU from module load until the process ends: a
+ * device array of KVC_NOALLOC_SCRATCH_BYTES.  Events whose
+ * kvc_workspace_bytes() exceeds that return KVC_ESCRATCH before anything is
+ * enqueued (the Qwen-7B-shaped 1792-head event needs about 29 MB; larger
+ * events use kvc_compress_event with a workspace).  Nothing is allocated and
+ * nothing is freed.  The GPU is the one `stream` runs on (the current device
+ * for the NULL stream); the first call on a GPU looks the array's address up
+ * once.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind (no call relies on them): calls that overlap in time on
+ * one GPU -- different streams, or different host threads without ordering
+ * -- race on it and must not be issued. */
+int kvc_compress_event_noalloc(const kvc_params* p, const void* q_win, const void* k,
+                               const void* v, const uint64_t* credit_in, void* k_out,
+                               void* v_out, uint64_t* credit_out, int32_t* kept_out,
+                               float* u_out, void* stream);
 
 /* Workspace bytes any entry point above needs for these parameters (0 when
  * the parameters are invalid).  Pure host function. */

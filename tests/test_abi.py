@@ -43,10 +43,28 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert kvc.abi_version() == kvc.ABI_VERSION == 2
-    for code in (0, 1, -1, -2, -3, -4, -5):
+    assert kvc.abi_version() == kvc.ABI_VERSION == 3
+    for code in (0, 1, -1, -2, -3, -4, -5, -6):
         assert kvc.strerror(code) and kvc.strerror(code) != "unknown status"
     assert kvc.strerror(-99) == "unknown status"
+
+
+def test_noalloc_rejects_events_past_its_scratch():
+    # Host-side checks of kvc_compress_event_noalloc return before any device
+    # call: invalid parameters, and events needing more than the library's
+    # scratch (the 128K-token event needs ~0.8 GB).
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+KVC_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == kvc.NOALLOC_SCRATCH_BYTES
+    L = kvc.lib()
+    big = _p(n_heads=256, T=131072, window=128, budget=4096, group=4, ema=True).to_c()
+    assert kvc.workspace_bytes(_p(n_heads=256, T=131072, window=128, budget=4096, group=4,
+                                  ema=True)) > kvc.NOALLOC_SCRATCH_BYTES
+    args = [None] * 10
+    assert L.kvc_compress_event_noalloc(ctypes.byref(big), *args) == kvc.ESCRATCH
+    bad = _p(window=0).to_c()
+    assert L.kvc_compress_event_noalloc(ctypes.byref(bad), *args) == -1
+    assert kvc.workspace_bytes(_p(n_heads=1792)) <= kvc.NOALLOC_SCRATCH_BYTES
 
 
 def test_header_version_matches_binding():
