@@ -21,6 +21,8 @@ WsLayout workspace_layout(const Derived& d) {
     return at;
   };
   L.stats = take(nh * size_t(d.R) * sizeof(float));  // row normalisers
+  // per-key-range partial normalisers of a split row-statistics pass
+  L.stats_part = take(d.rs_split > 1 ? nh * size_t(d.rs_split) * d.R * sizeof(float) : 0);
   L.u = take(nh * T * sizeof(float));
   L.score = take(nh * T * sizeof(float));
   L.cupd = take(d.ema ? nh * T * sizeof(uint64_t) : 0);
@@ -124,6 +126,7 @@ static int derive(const kvc_params* p, Derived* d) {
       p->seg_fixed > 0 ? int((int64_t(p->T) + p->seg_fixed - 1) / p->seg_fixed) - 1 : n_thr;
   d->n_thr = n_cut;
   d->seg_fixed = p->seg_fixed;
+  d->rs_split = score_pass1_splits(d->NH, d->R, d->T);
   d->quota_uniform = p->quota_mode == KVC_QUOTA_UNIFORM ? 1 : 0;
   d->vlen = p->valid_len;
   int64_t cap = int64_t(n_cut) + 1 + (p->seg_max > 0 ? p->T / p->seg_max : 0);
@@ -132,7 +135,7 @@ static int derive(const kvc_params* p, Derived* d) {
   d->s_cap = int(cap);
   const double scale = p->scale != 0.0f ? double(p->scale) : 1.0 / sqrt(double(p->head_dim));
   d->c_log2 = float(scale * 1.4426950408889634);  // scale * log2(e)
-  if (!(d->c_log2 >= 0x1p-60f)) return KVC_EINVAL;  // the score kernels need c >= 2^-60
+  if (!(d->c_log2 >= 0x1p-60f)) return KVC_EINVAL;  // scores below 2^-60 of a dot product: rejected
   d->eps_q = uint64_t(ceil(p->eps * 1099511627776.0));  // ceil(eps * 2^40)
   d->delta = p->delta;
   d->lam = p->lambda;
@@ -227,6 +230,7 @@ int kvc_score_window(const kvc_params* p, const void* q_win, const void* k, floa
   if (any_alias(in, 2, out, 2)) return KVC_EINVAL;
   char* w = static_cast<char*>(ws);
   return launch_status(launch_score(d, q_win, k, u, reinterpret_cast<float*>(w + L.stats),
+                                    reinterpret_cast<float*>(w + L.stats_part),
                                     hipStream_t(stream)));
 }
 
@@ -467,7 +471,8 @@ int kvc_compress_event(const kvc_params* p, const void* q_win, const void* k, co
   int32_t* seg_quota = reinterpret_cast<int32_t*>(w + L.seg_quota);
   int32_t* n_seg = reinterpret_cast<int32_t*>(w + L.n_seg);
 
-  rc = launch_status(launch_score(d, q_win, k, u, reinterpret_cast<float*>(w + L.stats), s));
+  rc = launch_status(launch_score(d, q_win, k, u, reinterpret_cast<float*>(w + L.stats),
+                                  reinterpret_cast<float*>(w + L.stats_part), s));
   if (rc != KVC_OK) return rc;
   rc = launch_status(launch_mass_segment(
       d, u, credit_in, score, cupd, reinterpret_cast<uint64_t*>(w + L.vp), seg_start, seg_quota,

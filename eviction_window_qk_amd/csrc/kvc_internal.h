@@ -27,6 +27,7 @@ struct Derived {
   float c_log2;                 // softmax scale * log2(e)
   uint64_t eps_q;               // ceil(eps * 2^40)
   double delta, lam, oml, beta, omb;
+  int rs_split;                 // key ranges the row-statistics pass is split into
   int seg_fixed;                // > 0: fixed-length raw segments (ablation)
   int quota_uniform;            // 1: every segment weighs 1 in the quotas (ablation)
   const int32_t* vlen;          // NULL or per-head valid length (device)
@@ -58,16 +59,36 @@ __host__ __device__ __forceinline__ Keep must_keep(int sinks, int recent, int K,
   return Keep{s, r, K - s - r};
 }
 
+// Key ranges the row-statistics pass splits each head's keys into, so that a
+// launch of heads with more than 128 query rows fills the chip: eight rounds
+// of workgroups at three waves per SIMD on the 256 CUs of an MI355X (fewer
+// rounds leave a longer tail; 2 -> 8 rounds: 128K-token event 9.75 -> 9.51
+// ms), in whole 64-key tiles of at least 2048 keys.  Heads with at most 128
+// rows stream K at the copy rate already and are not split (measured no
+// faster).  The partial statistics are merged by a log-sum-exp pass.
+inline int score_pass1_splits(int NH, int R, int T) {
+  if (R <= 128) return 1;
+  const int64_t wgs = int64_t(NH) * ((R + 255) / 256);  // four-wave workgroups of 256 rows
+  const int64_t target = 8 * (256 * 12 / 4);
+  if (wgs >= target) return 1;
+  int64_t s = (target + wgs - 1) / wgs;
+  const int64_t cap = T / 2048 > 1 ? T / 2048 : 1;
+  s = s < cap ? s : cap;
+  s = s < 64 ? s : 64;
+  const int64_t span = ((T + s - 1) / s + 63) / 64 * 64;  // no range left empty
+  return int((T + span - 1) / span);
+}
+
 // Workspace carve-up (byte offsets into the caller's buffer, 256-B aligned).
 struct WsLayout {
-  size_t stats, u, score, cupd, vp, seg_start, seg_quota, n_seg, seg_m, seg_a, seg_f, seg_q,
-      total;
+  size_t stats, stats_part, u, score, cupd, vp, seg_start, seg_quota, n_seg, seg_m, seg_a, seg_f,
+      seg_q, total;
 };
 WsLayout workspace_layout(const Derived& d);
 
 // Launchers (one per translation unit); return the first HIP error.
 hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u, float* stats,
-                        hipStream_t s);
+                        float* stats_part, hipStream_t s);
 hipError_t launch_mass_segment(const Derived& d, const float* u, const uint64_t* credit_in,
                                float* score, uint64_t* credit_upd, uint64_t* vp,
                                int32_t* seg_start, int32_t* seg_quota, int32_t* n_seg,

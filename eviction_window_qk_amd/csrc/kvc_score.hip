@@ -18,7 +18,10 @@
 //               each lane one row and 16 keys, so the running max m and sum l
 //               of 2^(x-m), x = <q,k>*scale*log2(e), stay lane-local; the two
 //               lane halves merge once at the end.  Output: the row
-//               normaliser b = m + log2(l) (log2 domain).
+//               normaliser b = m + log2(l) (log2 domain).  When a launch
+//               has too few heads to fill the chip, each head's keys are
+//               split into ranges whose partial normalisers k_rowmerge
+//               combines (b = log2 sum_s 2^b_s).
 //   k_colsum    keys stationary: each wave keeps 64 keys in registers (the B
 //               operand) and the workgroup streams the query rows through
 //               double-buffered LDS.  The accumulator gives each lane one key
@@ -28,8 +31,9 @@
 //   k_fill      positions seen by fewer than W queries take the maximum over
 //               the fully observed ones.
 //
-// Per score element the VALU work is one FMA, one exp2 and one add (plus half
-// a max in pass 1); the exp2 is the costliest of them, and on gfx950 the
+// Per score element the VALU work is one FMA, one exp2 and one add (pass 1
+// keeps a lazy reference maximum instead of a running one, so it needs no max
+// per element); the exp2 is the costliest of them, and on gfx950 the
 // vector ALU port, not the matrix core, bounds both passes.  Each wave issues
 // the MFMAs of one 32x32 block and then its softmax arithmetic; three waves
 // per SIMD (at most 168 VGPRs) let one wave's MFMAs run under another wave's
@@ -91,45 +95,54 @@ constexpr int kRsRows = kRsWaves * kRsRowBlocks * 32;   // rows per workgroup (2
 constexpr int kRsTile = 64;                             // keys per LDS tile (two 32-key blocks)
 constexpr int kRsThreads = 64 * kRsWaves;
 
-// Online max/sum update of one row (this lane's) with 16 new raw dot products.
-// m starts at the finite floor m_floor() instead of -inf, so no guards are
-// needed: the first visible key replaces it and the old l (0) is scaled by 0;
-// masked entries are -inf and add exp2(-inf) = 0.  The rescale factor is formed
-// from m - mx, which is exactly 0 while the maximum stands.
+// Sum of 2^(acc*c - m*c) over this lane's 16 dot products, -m*c given as nmc.
+__device__ __forceinline__ float exp_sum16(const f32x16& acc, float c, float nmc) {
+  float s0 = fast_exp2(__builtin_fmaf(acc[0], c, nmc));
+  float s1 = fast_exp2(__builtin_fmaf(acc[1], c, nmc));
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) {
+    s0 += fast_exp2(__builtin_fmaf(acc[r], c, nmc));
+    s1 += fast_exp2(__builtin_fmaf(acc[r + 1], c, nmc));
+  }
+  return s0 + s1;
+}
+
+// Running sum l of 2^(x*c - ref) over one row (this lane's) with 16 new raw
+// dot products x, the reference held as nmc = -ref (log2 units).  The
+// reference is not the running maximum: any value works for l as long as no
+// term overflows, so the block is summed against the current reference (one
+// FMA, one exp2 and one add per element) and the reference is raised only
+// when a lane's block sum passes 2^32 (a score 28 log2 units above it): then
+// the whole wave takes the block maximum as its new reference and rescales l.
+// nmc starts at 2^64, so the first visible block always takes that path;
+// masked entries are -inf and add exp2(-inf) = 0.  l stays below 2^18 keys x
+// 2^32 per key.  The row normaliser is b = ref + log2(l).
 template <bool MASK>
-__device__ __forceinline__ void row_update(f32x16 acc, float c, int t0, int h, int lim, float& m,
-                                           float& l) {
+__device__ __forceinline__ void row_update(f32x16 acc, float c, int t0, int h, int lim,
+                                           float& nmc, float& l) {
   if (MASK) {
     const int d = lim - t0 - 4 * h;
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (8 * (r >> 2) + (r & 3) > d) acc[r] = -INFINITY;
   }
-  float mx = fmaxf(fmaxf(m, acc[0]), acc[1]);
+  const float s = exp_sum16(acc, c, nmc);
+  if (__builtin_expect(__any(!(s <= 0x1p32f)), 0)) {
+    float mx = fmaxf(acc[0], acc[1]);
 #pragma unroll
-  for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
-  const float nb = -mx * c;
-  float s0 = fast_exp2(__builtin_fmaf(acc[0], c, nb));
-  float s1 = fast_exp2(__builtin_fmaf(acc[1], c, nb));
-#pragma unroll
-  for (int r = 2; r < 16; r += 2) {
-    s0 += fast_exp2(__builtin_fmaf(acc[r], c, nb));
-    s1 += fast_exp2(__builtin_fmaf(acc[r + 1], c, nb));
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+    const float nb = fminf(nmc, -mx * c);  // -max(ref, block maximum)
+    l = __builtin_fmaf(l, fast_exp2(nb - nmc), exp_sum16(acc, c, nb));
+    nmc = nb;
+  } else {
+    l += s;
   }
-  const float scale = fast_exp2((m - mx) * c);
-  l = __builtin_fmaf(l, scale, s0 + s1);
-  m = mx;
 }
-
-// Starting value of the running maximum: below every finite dot product the
-// inputs can produce in practice, with m_floor * c = -2^64 finite.  The host
-// rejects c < 2^-60, so the quotient is finite.
-__device__ __forceinline__ float m_floor(float c) { return -0x1p64f / c; }
 
 template <int D>
 struct RsCtx {
   u32x4 qop[kRsRowBlocks][D / 16];
-  float m[kRsRowBlocks], l[kRsRowBlocks];
+  float nmc[kRsRowBlocks], l[kRsRowBlocks];  // -reference (log2 units), running sum
   int lim[kRsRowBlocks];
   int lo[kRsRowBlocks], hi[kRsRowBlocks];  // wave-uniform min/max of lim per row block
 };
@@ -157,9 +170,9 @@ template <int D>
 __device__ __forceinline__ void rs_update(RsCtx<D>& cx, int rb, const f32x16& acc, int t0,
                                           float c, int h) {
   if (t0 + 31 <= cx.lo[rb])
-    row_update<false>(acc, c, t0, h, cx.lim[rb], cx.m[rb], cx.l[rb]);
+    row_update<false>(acc, c, t0, h, cx.lim[rb], cx.nmc[rb], cx.l[rb]);
   else
-    row_update<true>(acc, c, t0, h, cx.lim[rb], cx.m[rb], cx.l[rb]);
+    row_update<true>(acc, c, t0, h, cx.lim[rb], cx.nmc[rb], cx.l[rb]);
 }
 
 // One 32-key block: fragments from LDS, MFMAs for the row blocks that see
@@ -198,6 +211,8 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 2 : 3))) void k_rowstats(Derived P, const u32x4* __restrict__ q,
                                                             const u32x4* __restrict__ k,
                                                             float* __restrict__ rowb) {
+  // rowb: [NH][R] normalisers, or with P.rs_split > 1 the partial ones
+  // [NH][R][rs_split] of key range s = [s*span, min(T, (s+1)*span)).
   constexpr int kPerRow = D / 8;        // u32x4 per row
   constexpr int kStride = kPerRow + 1;  // LDS row stride (one pad piece)
   constexpr int kThreads = 64 * NW;
@@ -206,8 +221,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2
   __shared__ u32x4 ks[2][kRsTile * kStride];
 
   const int groups = (P.R + kRows - 1) / kRows;
+  const int S = P.rs_split;
   const unsigned lb = xcd_logical_block();
-  const int n = lb / groups, grp = lb % groups;
+  const int n = lb / (groups * S), grp = lb % groups, split = (lb / groups) % S;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, h = lane >> 5;
   const Span sp = head_span(P, n);  // real tokens of a left-padded head
@@ -225,40 +241,54 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2
     cx.lo[rb] = wave_min(cx.lim[rb]);
     cx.hi[rb] = wave_max(cx.lim[rb]);
     load_rows_op<D>(q + size_t(n) * R * kPerRow, rc, h, cx.qop[rb]);
-    cx.m[rb] = m_floor(c);
+    cx.nmc[rb] = 0x1p64f;
     cx.l[rb] = 0.0f;
   }
 
+  // This workgroup's key range: whole tiles, so no tile straddles two ranges.
+  const int span = ((T + S - 1) / S + kRsTile - 1) / kRsTile * kRsTile;
+  const int t_lo = split * span;
+  const int t_hi = t_lo + span < T ? t_lo + span : T;
   const u32x4* kn = k + (size_t(n) * P.TS + sp.off) * kPerRow;
-  const int n_tiles = (T + kRsTile - 1) / kRsTile;
+  const int n_tiles = t_hi > t_lo ? (t_hi - t_lo + kRsTile - 1) / kRsTile : 0;
+  // A tile is kRsTile whole key rows, one contiguous run of kRsTile*kPerRow
+  // pieces: thread x loads pieces x, x + kThreads, ...  (a uniform tile
+  // pointer plus one lane offset).  Only a tile running past T clamps its
+  // rows (those keys are masked; the clamp keeps the loads in bounds).
   auto fetch = [&](int kt, u32x4 (&pre)[kLoads]) {
+    const int t0 = t_lo + kt * kRsTile;
+    const u32x4* tile = kn + size_t(t0) * kPerRow;
+    if (t0 + kRsTile <= T) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      int t = kt * kRsTile + e / kPerRow;
-      t = t < T ? t : T - 1;  // rows past T are masked; keep the load in bounds
-      pre[i] = kn[size_t(t) * kPerRow + e % kPerRow];
+      for (int i = 0; i < kLoads; ++i) pre[i] = tile[threadIdx.x + i * kThreads];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int e = threadIdx.x + i * kThreads;
+        const int row = t0 + e / kPerRow < T ? e / kPerRow : T - 1 - t0;
+        pre[i] = tile[row * kPerRow + e % kPerRow];
+      }
     }
   };
   auto stash = [&](int buf, const u32x4 (&pre)[kLoads]) {
+    u32x4* dst = ks[buf] + (threadIdx.x / kPerRow) * kStride + threadIdx.x % kPerRow;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      ks[buf][(e / kPerRow) * kStride + e % kPerRow] = pre[i];
-    }
+    for (int i = 0; i < kLoads; ++i) dst[i * (kThreads / kPerRow) * kStride] = pre[i];
   };
 
   u32x4 pre[kLoads];
-  fetch(0, pre);
-  stash(0, pre);
-  if (n_tiles > 1) fetch(1, pre);
+  if (n_tiles > 0) {
+    fetch(0, pre);
+    stash(0, pre);
+    if (n_tiles > 1) fetch(1, pre);
+  }
   __syncthreads();
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const u32x4* buf = ks[kt & 1];
     if (wave_active) {
-      rs_block<D>(cx, buf, 0, kt * kRsTile, c, j, h);
-      rs_block<D>(cx, buf, 1, kt * kRsTile + 32, c, j, h);
+      rs_block<D>(cx, buf, 0, t_lo + kt * kRsTile, c, j, h);
+      rs_block<D>(cx, buf, 1, t_lo + kt * kRsTile + 32, c, j, h);
     }
     if (kt + 1 < n_tiles) {
       stash((kt + 1) & 1, pre);
@@ -268,18 +298,38 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2
   }
   if (!wave_active) return;
 
-  // Merge the two lane halves (same row, different keys) and write b.  Key 0
-  // is visible to every row, so at least one half holds a real maximum; a
-  // half that saw no key has l = 0 and m = m_floor.
+  // Merge the two lane halves (same row, different keys) onto the larger
+  // reference and write b = ref + log2(l).  Key 0 is visible to every row, so
+  // the first key range always has a sum; a half (or a range) that saw no key
+  // has l = 0 and nmc = 2^64, and a range with no key gets b = -inf.
 #pragma unroll
   for (int rb = 0; rb < kRsRowBlocks; ++rb) {
-    const float mo = __shfl_xor(cx.m[rb], 32);
+    const float no = __shfl_xor(cx.nmc[rb], 32);
     const float lo = __shfl_xor(cx.l[rb], 32);
-    const float mm = fmaxf(cx.m[rb], mo);
-    const float ll = cx.l[rb] * fast_exp2((cx.m[rb] - mm) * c) + lo * fast_exp2((mo - mm) * c);
+    const float nm = fminf(cx.nmc[rb], no);
+    const float ll = cx.l[rb] * fast_exp2(nm - cx.nmc[rb]) + lo * fast_exp2(nm - no);
     const int r = row0 + rb * 32 + j;
-    if (h == 0 && r < R) rowb[size_t(n) * R + r] = mm * c + __log2f(ll);
+    if (h == 0 && r < R) rowb[(size_t(n) * R + r) * S + split] = __log2f(ll) - nm;
   }
+}
+
+// Row normaliser from the partial ones of the key ranges: b = M +
+// log2(sum_s 2^(b_s - M)), M = max_s b_s (finite: the first range holds key 0,
+// which every row sees; a range with no visible key has b_s = -inf and adds
+// 2^-inf = 0).  A row's partials are contiguous, so its loads go out together.
+__global__ __launch_bounds__(256) void k_rowmerge(Derived P, const float* __restrict__ part,
+                                                  float* __restrict__ rowb) {
+  const int S = P.rs_split;
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= size_t(P.NH) * P.R) return;
+  const float* pn = part + i * S;
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pn[s]);
+  float sum = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) sum += fast_exp2(pn[s] - M);
+  rowb[i] = M + __log2f(sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -587,29 +637,39 @@ __global__ __launch_bounds__(NT) void k_fill(Derived P, float* __restrict__ u) {
 }  // namespace
 
 hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u, float* stats,
-                        hipStream_t s) {
+                        float* stats_part, hipStream_t s) {
   const u32x4* qv = static_cast<const u32x4*>(q);
   const u32x4* kv = static_cast<const u32x4*>(k);
   const bool small_r = d.R <= 2 * kRsRowBlocks * 32;  // two-wave pass-1 workgroups
   const int rs_rows = small_r ? 2 * kRsRowBlocks * 32 : kRsRows;
-  const unsigned g_rs = unsigned((d.R + rs_rows - 1) / rs_rows) * unsigned(d.NH);
-  const unsigned g_cs = unsigned((d.T + kCsKeys - 1) / kCsKeys) * unsigned(d.NH);
-  // Small windows (at most kResBlocks padded 32-row blocks): queries resident in LDS.
+  const unsigned g_rs =
+      unsigned((d.R + rs_rows - 1) / rs_rows) * unsigned(d.NH) * unsigned(d.rs_split);
+  float* rs_out = d.rs_split > 1 ? stats_part : stats;
   const int cs_chunks = (d.T + kCsKeys - 1) / kCsKeys;
+  const unsigned g_cs = unsigned(cs_chunks) * unsigned(d.NH);
+  // Small windows (at most kResBlocks padded 32-row blocks) on launches with
+  // chunks to spare: queries resident in LDS.
   const bool resident = d.G * ((d.W + 31) / 32) <= kResBlocks && int64_t(cs_chunks) * d.NH >= 8192;
   const int cpw = 8;  // measured: 2, 4, 8, 16, 32 -> 8 fastest
   const unsigned g_res = unsigned((cs_chunks + cpw - 1) / cpw) * unsigned(d.NH);
   if (d.D == 128) {
-    if (small_r) k_rowstats<128, 2><<<g_rs, 128, 0, s>>>(d, qv, kv, stats);
-    else k_rowstats<128, kRsWaves><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, stats);
+    if (small_r) k_rowstats<128, 2><<<g_rs, 128, 0, s>>>(d, qv, kv, rs_out);
+    else k_rowstats<128, kRsWaves><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, rs_out);
+  } else {
+    if (small_r) k_rowstats<64, 2><<<g_rs, 128, 0, s>>>(d, qv, kv, rs_out);
+    else k_rowstats<64, kRsWaves><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, rs_out);
+  }
+  if (d.rs_split > 1) {
+    const size_t rows = size_t(d.NH) * d.R;
+    k_rowmerge<<<unsigned((rows + 255) / 256), 256, 0, s>>>(d, stats_part, stats);
+  }
+  if (d.D == 128) {
     if (d.head_agg == KVC_AGG_SUM)
       resident ? k_colsum_resident<128><<<g_res, kCsThreads, 0, s>>>(d, qv, kv, stats, u, cpw)
                : k_colsum<128, true><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
     else
       k_colsum<128, false><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
   } else {
-    if (small_r) k_rowstats<64, 2><<<g_rs, 128, 0, s>>>(d, qv, kv, stats);
-    else k_rowstats<64, kRsWaves><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, stats);
     if (d.head_agg == KVC_AGG_SUM)
       resident ? k_colsum_resident<64><<<g_res, kCsThreads, 0, s>>>(d, qv, kv, stats, u, cpw)
                : k_colsum<64, true><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
