@@ -86,6 +86,16 @@ __device__ __forceinline__ void load_rows_op(const u32x4* __restrict__ base, int
 
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Completes the loads of a register-resident MFMA operand here, before the
+// main loop.  Without it the compiler waits for them at their first use
+// inside the loop on every iteration, and since the vector-memory counter
+// retires in order, those waits also wait for the next tile's prefetch.
+template <int N>
+__device__ __forceinline__ void operand_ready(const u32x4 (&op)[N]) {
+#pragma unroll
+  for (int s = 0; s < N; ++s) asm volatile("" ::"v"(op[s]));
+}
+
 // ---------------------------------------------------------------------------
 // pass 1: row statistics
 // ---------------------------------------------------------------------------
@@ -241,6 +251,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2
     cx.lo[rb] = wave_min(cx.lim[rb]);
     cx.hi[rb] = wave_max(cx.lim[rb]);
     load_rows_op<D>(q + size_t(n) * R * kPerRow, rc, h, cx.qop[rb]);
+    operand_ready(cx.qop[rb]);
     cx.nmc[rb] = 0x1p64f;
     cx.l[rb] = 0.0f;
   }
@@ -495,6 +506,7 @@ __global__ __launch_bounds__(kCsThreads, SUM ? 3 : 2) void k_colsum(Derived P, c
     int t = key_base + kb * 32 + j;
     t = t < T ? t : T - 1;  // keys past T are never written
     load_rows_op<D>(kn, t, h, cx.kop[kb]);
+    operand_ready(cx.kop[kb]);
   }
   const u32x4* qn = q + size_t(n) * R * kPerRow;
 
