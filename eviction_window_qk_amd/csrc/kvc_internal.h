@@ -67,7 +67,7 @@ __host__ __device__ __forceinline__ Keep must_keep(int sinks, int recent, int K,
 // rows stream K at the copy rate already and are not split (measured no
 // faster).  The partial statistics are merged by a log-sum-exp pass.
 inline int score_pass1_splits(int NH, int R, int T) {
-  if (R <= 128) return 1;
+  if (R <= 128 || NH < 1) return 1;
   const int64_t wgs = int64_t(NH) * ((R + 255) / 256);  // four-wave workgroups of 256 rows
   const int64_t target = 8 * (256 * 12 / 4);
   if (wgs >= target) return 1;
