@@ -538,24 +538,32 @@ __global__ __launch_bounds__(kCsThreads, SUM ? 3 : 2) void k_colsum(Derived P, c
 // Pass 2 for heads with at most kResBlocks 32-row blocks (W*G <= 128 after
 // padding each query head's window to 32 rows), SUM aggregation, on launches
 // with chunks to spare: the whole window (queries and row normalisers) stays
-// in LDS, so a workgroup walks cpw consecutive 256-key chunks of one head
-// with no barrier between them instead of re-streaming the queries for each
-// chunk (16K-token global event: score stage 1.87 -> 1.76 ms).  The row
+// in LDS, so a workgroup walks cpw consecutive chunks of 64*NW keys of one
+// head with no barrier between them instead of re-streaming the queries for
+// each chunk (16K-token global event: score stage 1.87 -> 1.76 ms).  The row
 // blocks are visited in the same order as in k_colsum, so the sums are
-// identical.
+// identical.  Two shapes: four waves and at most four padded 32-row blocks
+// (W*G <= 128), several workgroups per CU; and twelve waves and at most
+// sixteen blocks (W*G <= 512: 139 KB of queries), one workgroup per CU that
+// walks a whole head -- long caches with a few hundred query rows per head,
+// whose workgroups would otherwise spend much of their short lives starting
+// up (staging the normalisers, loading the key operands, filling the query
+// pipeline).
 constexpr int kResBlocks = 4;
+constexpr int kWideWaves = 12, kWideBlocks = 16;
 
-template <int D>
-__global__ __launch_bounds__(kCsThreads, 3) void k_colsum_resident(Derived P, const u32x4* __restrict__ q,
-                                                                   const u32x4* __restrict__ k,
-                                                                   const float* __restrict__ rowb,
-                                                                   float* __restrict__ u, int cpw) {
+template <int D, int NW, int NB>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void k_colsum_resident(
+    Derived P, const u32x4* __restrict__ q, const u32x4* __restrict__ k,
+    const float* __restrict__ rowb, float* __restrict__ u, int cpw) {
   constexpr int kPerRow = D / 8;
   constexpr int kStride = kPerRow + 1;
-  __shared__ u32x4 qs[kResBlocks * 32 * kStride];
-  __shared__ __align__(16) float bsh[kResBlocks * 32];
+  constexpr int kThreads = 64 * NW;
+  constexpr int kChunk = NW * kScoreKeysPerWave;  // keys per chunk
+  __shared__ u32x4 qs[NB * 32 * kStride];
+  __shared__ __align__(16) float bsh[NB * 32];
 
-  const int chunks = (P.T + kCsKeys - 1) / kCsKeys;
+  const int chunks = (P.T + kChunk - 1) / kChunk;
   const int groups = (chunks + cpw - 1) / cpw;
   const unsigned lb = xcd_logical_block();
   const int n = lb / groups, grp = lb % groups;
@@ -564,17 +572,17 @@ __global__ __launch_bounds__(kCsThreads, 3) void k_colsum_resident(Derived P, co
   const Span sp = head_span(P, n);  // real tokens of a left-padded head
   const int T = sp.T, W = P.W, R = P.R, G = P.G;
   const int c0 = grp * cpw;
-  if (c0 * kCsKeys >= T) return;  // whole workgroup: no real key in its chunks
+  if (c0 * kChunk >= T) return;  // whole workgroup: no real key in its chunks
   const float c = P.c_log2;
   const int n_rb = (W + 31) / 32;
-  const int n_blocks = G * n_rb;  // <= kResBlocks (host)
+  const int n_blocks = G * n_rb;  // <= NB (host)
 
-  for (int i = threadIdx.x; i < n_blocks * 32; i += kCsThreads) {
+  for (int i = threadIdx.x; i < n_blocks * 32; i += kThreads) {
     const int g = i / (n_rb * 32), w = i % (n_rb * 32);
     bsh[i] = w < W ? rowb[size_t(n) * R + g * W + w] : INFINITY;  // +inf: p = 0
   }
   const u32x4* qn = q + size_t(n) * R * kPerRow;
-  for (int e = threadIdx.x; e < n_blocks * 32 * kPerRow; e += kCsThreads) {
+  for (int e = threadIdx.x; e < n_blocks * 32 * kPerRow; e += kThreads) {
     const int blk = e / (32 * kPerRow);
     const int g = blk / n_rb;
     int w = (blk % n_rb) * 32 + (e / kPerRow) % 32;
@@ -585,8 +593,8 @@ __global__ __launch_bounds__(kCsThreads, 3) void k_colsum_resident(Derived P, co
 
   const u32x4* kn = k + (size_t(n) * P.TS + sp.off) * kPerRow;
   float* un = u + size_t(n) * P.T + sp.off;
-  for (int ch = c0; ch < c0 + cpw && ch * kCsKeys < T; ++ch) {
-    const int key_base = ch * kCsKeys + wave * kScoreKeysPerWave;
+  for (int ch = c0; ch < c0 + cpw && ch * kChunk < T; ++ch) {
+    const int key_base = ch * kChunk + wave * kScoreKeysPerWave;
     CsCtx<D> cx;
     cx.key0 = key_base + j;
 #pragma unroll
@@ -659,11 +667,20 @@ hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u
   float* rs_out = d.rs_split > 1 ? stats_part : stats;
   const int cs_chunks = (d.T + kCsKeys - 1) / kCsKeys;
   const unsigned g_cs = unsigned(cs_chunks) * unsigned(d.NH);
+  const int nb_pad = d.G * ((d.W + 31) / 32);  // padded 32-row blocks per head
   // Small windows (at most kResBlocks padded 32-row blocks) on launches with
   // chunks to spare: queries resident in LDS.
-  const bool resident = d.G * ((d.W + 31) / 32) <= kResBlocks && int64_t(cs_chunks) * d.NH >= 8192;
+  const bool resident = nb_pad <= kResBlocks && int64_t(cs_chunks) * d.NH >= 8192;
   const int cpw = 8;  // measured: 2, 4, 8, 16, 32 -> 8 fastest
   const unsigned g_res = unsigned((cs_chunks + cpw - 1) / cpw) * unsigned(d.NH);
+  // Up to kWideBlocks blocks: one twelve-wave workgroup per CU, each walking
+  // its share of a head (at least four 768-key chunks, else the streamed
+  // kernel).
+  const int w_chunks = (d.T + kWideWaves * kScoreKeysPerWave - 1) / (kWideWaves * kScoreKeysPerWave);
+  const int w_groups = d.NH >= 256 ? 1 : (256 + d.NH - 1) / d.NH;  // workgroups per head
+  const int w_cpw = (w_chunks + w_groups - 1) / w_groups;
+  const bool wide = !resident && d.head_agg == KVC_AGG_SUM && nb_pad <= kWideBlocks && w_cpw >= 4;
+  const unsigned g_wide = unsigned((w_chunks + w_cpw - 1) / w_cpw) * unsigned(d.NH);
   if (d.D == 128) {
     if (small_r) k_rowstats<128, 2><<<g_rs, 128, 0, s>>>(d, qv, kv, rs_out);
     else k_rowstats<128, kRsWaves><<<g_rs, kRsThreads, 0, s>>>(d, qv, kv, rs_out);
@@ -676,14 +693,18 @@ hipError_t launch_score(const Derived& d, const void* q, const void* k, float* u
     k_rowmerge<<<unsigned((rows + 255) / 256), 256, 0, s>>>(d, stats_part, stats);
   }
   if (d.D == 128) {
-    if (d.head_agg == KVC_AGG_SUM)
-      resident ? k_colsum_resident<128><<<g_res, kCsThreads, 0, s>>>(d, qv, kv, stats, u, cpw)
+    if (wide)
+      k_colsum_resident<128, kWideWaves, kWideBlocks><<<g_wide, 64 * kWideWaves, 0, s>>>(d, qv, kv, stats, u, w_cpw);
+    else if (d.head_agg == KVC_AGG_SUM)
+      resident ? k_colsum_resident<128, kCsWaves, kResBlocks><<<g_res, kCsThreads, 0, s>>>(d, qv, kv, stats, u, cpw)
                : k_colsum<128, true><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
     else
       k_colsum<128, false><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
   } else {
-    if (d.head_agg == KVC_AGG_SUM)
-      resident ? k_colsum_resident<64><<<g_res, kCsThreads, 0, s>>>(d, qv, kv, stats, u, cpw)
+    if (wide)
+      k_colsum_resident<64, kWideWaves, kWideBlocks><<<g_wide, 64 * kWideWaves, 0, s>>>(d, qv, kv, stats, u, w_cpw);
+    else if (d.head_agg == KVC_AGG_SUM)
+      resident ? k_colsum_resident<64, kCsWaves, kResBlocks><<<g_res, kCsThreads, 0, s>>>(d, qv, kv, stats, u, cpw)
                : k_colsum<64, true><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);
     else
       k_colsum<64, false><<<g_cs, kCsThreads, 0, s>>>(d, qv, kv, stats, u);

@@ -126,3 +126,32 @@ def test_resident_column_sums_ragged():
     assert not np.isnan(u_gpu).any()
     check_steps2to5_ragged(pd, u_gpu, k, v, None, heads, lengths)
     print("[case] resident ragged: sampled heads ok", flush=True)
+
+
+@pytest.mark.gpu
+def test_wide_resident_column_sums_agree_with_streamed():
+    """Windows of up to sixteen padded 32-row blocks on long caches take the
+    twelve-wave LDS-resident pass 2 (one workgroup per CU walking a share of a
+    head); the same heads in a small launch take the streamed kernel.  Their
+    usage must have the same bits, and sampled heads match the oracle."""
+    import numpy as np
+    import torch
+    from oracle import ams
+    from parity_utils import assert_usage_close, dev_bf16, kvc_params, oracle_params, widen
+    NH, G, W, d, T, K = 16, 4, 128, 64, 49152, 2000   # 16 heads x 64 chunks of 768 keys
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
+    q, k, _ = synth.random_small(8080, NH, G, W, d, T)
+    dq, dk = dev_bf16(q), dev_bf16(k)
+    print(f"[case] wide resident pass 2: NH={NH} G={G} W={W} d={d} T={T}", flush=True)
+    u_all = kvc.score_window(kvc_params(pd, NH), dq, dk)
+    for sub in ([0, 1], [9, 15]):
+        idx = torch.tensor(sub, device="cuda")
+        u_sub = kvc.score_window(kvc_params(pd, len(sub)), dq[idx].contiguous(), dk[idx].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(u_sub.view(torch.int32), u_all[idx].view(torch.int32)), sub
+    u_gpu = u_all.cpu().numpy()
+    op = oracle_params(pd)
+    for n in (0, 15):
+        assert_usage_close(u_gpu[n], ams.window_usage(widen(q[n]), widen(k[n, :T]), op),
+                           f"wide resident head {n}")
+    print("[case] wide resident pass 2: identical bits, sampled heads within tolerance", flush=True)
