@@ -26,7 +26,9 @@ def test_headline_records_are_current():
     mf = bench.recorded_mfma(HEADLINE)
     assert tr is not None and tr > 0
     assert mf is not None
-    assert set(mf["mfma_busy"]) == {"k_rowstats", "k_colsum"}
+    # pass 1, and pass 2 in whichever variant the workload takes (streamed or LDS-resident)
+    assert len(mf["mfma_busy"]) == 2 and "k_rowstats" in mf["mfma_busy"]
+    assert any(k.startswith("k_colsum") for k in mf["mfma_busy"])
     assert all(0.0 < v < 1.0 for v in mf["mfma_busy"].values())
 
 
