@@ -73,15 +73,18 @@ __device__ __forceinline__ unsigned xcd_logical_block() {
 
 // Operand layout.  Lane (j = lane & 31, h = lane >> 5) supplies row/column j
 // of a 32-wide MFMA operand and, for k-step s, head-dim elements
-// [h*D/2 + 8s, h*D/2 + 8s + 8).  Any bijection of the head dimension gives the
-// same dot product as long as both operands use it; this one makes a lane's
-// share of a row one contiguous run.  Accumulator element r of a 32x32 tile
+// [16s + 8h, 16s + 8h + 8).  Any bijection of the head dimension gives the
+// same dot product as long as both operands use it; this one puts the two
+// lanes of a row on adjacent 16-byte pieces, so one load instruction of a
+// register operand touches 32 cache lines rather than 64 (32 bytes each).
+// In LDS (rows padded by one 16-byte piece) the pieces of eight consecutive
+// rows still fall in distinct banks.  Accumulator element r of a 32x32 tile
 // is at (row 8(r/4) + 4h + (r%4), column j).
 template <int D>
 __device__ __forceinline__ void load_rows_op(const u32x4* __restrict__ base, int row, int h,
                                              u32x4 (&op)[D / 16]) {
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) op[s] = base[size_t(row) * (D / 8) + h * (D / 16) + s];
+  for (int s = 0; s < D / 16; ++s) op[s] = base[size_t(row) * (D / 8) + 2 * s + h];
 }
 
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -162,7 +165,7 @@ __device__ __forceinline__ void load_frags(const u32x4* __restrict__ buf, int bl
                                            u32x4 (&f)[D / 16]) {
   constexpr int kStride = D / 8 + 1;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) f[s] = buf[(blk * 32 + j) * kStride + h * (D / 16) + s];
+  for (int s = 0; s < D / 16; ++s) f[s] = buf[(blk * 32 + j) * kStride + 2 * s + h];
 }
 
 __device__ __forceinline__ int wave_min(int x) {
