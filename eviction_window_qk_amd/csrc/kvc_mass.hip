@@ -21,6 +21,8 @@
 //    mass as Q44.
 #pragma clang fp contract(off)
 
+#include <type_traits>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -141,6 +143,53 @@ __device__ __forceinline__ float pooled(const float* __restrict__ tile, int t_ba
   return acc / float(hi - lo + 1);
 }
 
+// The same pooled usage at a position whose whole window lies inside the
+// cache, for a compile-time half-width H: the window's reads all issue before
+// the sum (which keeps its ascending order from +0.0).  The average divides
+// by the fixed count n = 2H+1 through its reciprocal y = RN(1/n): with
+// q = RN(a*y), RN(q + fma(-n, q, a)*y) is the correctly rounded a/n for every
+// float a in [2^-80, 2^100] (no intermediate is subnormal there; checked
+// exhaustively against IEEE division for every n <= 63).  Other sums (zero,
+// tiny, huge, non-finite) take the division.
+template <int H>
+__device__ __forceinline__ float pooled_interior(const float* __restrict__ x, int t, int mode) {
+  float v[2 * H + 1];
+#pragma unroll
+  for (int j = 0; j <= 2 * H; ++j) v[j] = x[t - H + j];
+  if (mode == KVC_POOL_MAX) {
+    float m = v[0];
+#pragma unroll
+    for (int j = 1; j <= 2 * H; ++j) m = fmaxf(m, v[j]);
+    return m;
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j <= 2 * H; ++j) acc = acc + v[j];
+  constexpr float n = float(2 * H + 1);
+  constexpr float y = 1.0f / n;
+  if (acc >= 0x1p-80f && acc <= 0x1p100f) {
+    const float q = acc * y;
+    return __builtin_fmaf(__builtin_fmaf(-n, q, acc), y, q);
+  }
+  return acc / n;
+}
+
+// a / d correctly rounded, for a >= 0 and a divisor d > 0 that is fixed for
+// the whole head (both far from underflow and overflow), from y = RN(1/d)
+// taken once: q = RN(a*y) is within one ulp of a/d, the residual a - d*q is
+// exact in one FMA, and RN(q + residual*y) is the correctly rounded quotient
+// (Markstein's theorem for a reciprocal within half an ulp).  Three fp64
+// operations instead of a full division per position.
+struct Divisor {
+  double d, y;
+};
+__device__ __forceinline__ Divisor make_divisor(double d) { return Divisor{d, 1.0 / d}; }
+__device__ __forceinline__ double div_rn(double a, Divisor D) {
+  const double q = a * D.y;
+  const double r = __builtin_fma(-D.d, q, a);
+  return __builtin_fma(r, D.y, q);
+}
+
 // Sum of v over [a, b] (inclusive, may be empty) from the inclusive prefix.
 __device__ __forceinline__ uint64_t range_sum(const uint64_t* __restrict__ P, int a, int b) {
   if (a > b) return 0;
@@ -209,34 +258,56 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   // one tile of NT*kSweep positions (plus the pooling halo) through LDS
   uint64_t part = 0;
   const int h = P.pool_h;
-  for (int t_base = 0; t_base < T; t_base += NT * kSweep) {
-    const int span = NT * kSweep + 2 * h;  // <= NT * (kSweep + 1): 2h <= 62 < NT
-    // Every load of the tile is issued before any is stored: clamped indices
-    // instead of branches (slots outside [0, T) hold a copy never read).
+  // Every load of a tile is issued before any is stored: clamped indices
+  // instead of branches (slots outside [0, T) hold a copy never read).  The
+  // next tile's loads go out before this tile is pooled.  The default
+  // pooling kernel (7, half-width 3) runs with its half-width known at
+  // compile time, so each interior window is read at once (128K-token event:
+  // pooling sweep 87 -> 53 us); edges and other kernels take the loop.
+  auto pool_sweep = [&](auto half_width) {
+    constexpr int HC = decltype(half_width)::value;  // < 0: only the runtime h
     float tv[kSweep + 1];
+    auto load_tile = [&](int t_base) {
 #pragma unroll
-    for (int k = 0; k <= kSweep; ++k) {
-      int t = t_base - h + tid + k * NT;
-      t = t < 0 ? 0 : (t >= T ? T - 1 : t);
-      tv[k] = un[t];
-    }
-    __syncthreads();  // previous tile consumed
+      for (int k = 0; k <= kSweep; ++k) {
+        int t = t_base - h + tid + k * NT;
+        t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+        tv[k] = un[t];
+      }
+    };
+    load_tile(0);
+    for (int t_base = 0; t_base < T; t_base += NT * kSweep) {
+      const int span = NT * kSweep + 2 * h;  // <= NT * (kSweep + 1): 2h <= 62 < NT
+      __syncthreads();  // previous tile consumed
 #pragma unroll
-    for (int k = 0; k <= kSweep; ++k)
-      if (tid + k * NT < span) sh.u.tile[tid + k * NT] = tv[k];
-    __syncthreads();
+      for (int k = 0; k <= kSweep; ++k)
+        if (tid + k * NT < span) sh.u.tile[tid + k * NT] = tv[k];
+      __syncthreads();
+      load_tile(t_base + NT * kSweep);  // past the end: clamped copies, never stored
 #pragma unroll
-    for (int k = 0; k < kSweep; ++k) {
-      const int t = t_base + k * NT + tid;
-      if (t < T) {
-        const float ub = pooled(sh.u.tile, t_base, T, t, h, P.pool_mode);
-        sc[t] = ub;
-        const uint64_t w = usage_q(ub);
-        if (one_seg && (t <= s_end || t >= r_beg)) mk_part += w;
-        part += w;
+      for (int k = 0; k < kSweep; ++k) {
+        const int t = t_base + k * NT + tid;
+        if (t < T) {
+          float ub;
+          if constexpr (HC >= 0) {
+            ub = t >= HC && t + HC <= T - 1
+                     ? pooled_interior<HC>(sh.u.tile + (HC - t_base), t, P.pool_mode)
+                     : pooled(sh.u.tile, t_base, T, t, h, P.pool_mode);
+          } else {
+            ub = pooled(sh.u.tile, t_base, T, t, h, P.pool_mode);
+          }
+          sc[t] = ub;
+          const uint64_t w = usage_q(ub);
+          if (one_seg && (t <= s_end || t >= r_beg)) mk_part += w;
+          part += w;
+        }
       }
     }
-  }
+  };
+  if (h == 3)
+    pool_sweep(std::integral_constant<int, 3>{});
+  else
+    pool_sweep(std::integral_constant<int, -1>{});
   const uint64_t w_total = block_sum_u64<NT>(part, sh);
   uint64_t v_total = w_total;  // C(T-1)
 
@@ -244,48 +315,58 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
   // the mixed mass v is formed where it is consumed (the prefix scan, or the
   // one-segment sums).
   uint64_t* cu = P.ema ? credit_upd + size_t(n) * P.T + sp.off : nullptr;
-  const double wd = double(w_total);
+  const Divisor wd = make_divisor(double(w_total));
   uint64_t c_total = 0;
-  double cd = 0.0;
+  Divisor cd{0.0, 0.0};
   auto mixed = [&](uint64_t w, uint64_t cq) -> uint64_t {
-    const double mq = double(w) / wd;
-    const double nc = c_total ? double(cq) / cd : 0.0;
+    const double mq = div_rn(double(w), wd);
+    const double nc = c_total ? div_rn(double(cq), cd) : 0.0;
     const double mix = (P.beta * mq) + (P.omb * nc);
     return uint64_t(floor(mix * 0x1p44));
   };
   if (P.ema) {
     const uint64_t* ci = credit_in ? credit_in + size_t(n) * P.n_prev : nullptr;
     part = 0;
-    for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
-      float sv[kSweep];
-      uint64_t cin[kSweep];
+    // Loads first, clamped (no branches), and one stride ahead of the sweep.
+    float sv[kSweep], sv_next[kSweep];
+    uint64_t cin[kSweep], cin_next[kSweep];
+    auto load_ema = [&](int t0, float (&s_)[kSweep], uint64_t (&c_)[kSweep]) {
 #pragma unroll
-      for (int k = 0; k < kSweep; ++k) {  // loads first, clamped (no branches)
+      for (int k = 0; k < kSweep; ++k) {
         const int t = t0 + k * NT;
-        sv[k] = sc[t < T ? t : T - 1];
-        cin[k] = 0;
+        s_[k] = sc[t < T ? t : T - 1];
+        c_[k] = 0;
       }
       if (P.n_prev > 0) {
 #pragma unroll
         for (int k = 0; k < kSweep; ++k) {
           const int t = t0 + k * NT;
-          cin[k] = ci[t < P.n_prev ? t : P.n_prev - 1];
+          c_[k] = ci[t < P.n_prev ? t : P.n_prev - 1];
         }
       }
+    };
+    load_ema(tid, sv, cin);
+    for (int t0 = tid; t0 < T; t0 += NT * kSweep) {
+      load_ema(t0 + NT * kSweep, sv_next, cin_next);  // past the end: clamped copies, unused
 #pragma unroll
       for (int k = 0; k < kSweep; ++k) {
         const int t = t0 + k * NT;
         if (t >= T) continue;
-        const double mq = double(usage_q(sv[k])) / wd;
+        const double mq = div_rn(double(usage_q(sv[k])), wd);
         const double c = t < P.n_prev ? double(cin[k]) * 0x1p-44 : floor(mq * 0x1p44) * 0x1p-44;
         const double c_new = (P.lam * c) + (P.oml * mq);
         const uint64_t cq = uint64_t(floor(c_new * 0x1p44));
         cu[t] = cq;
         part += cq;
       }
+#pragma unroll
+      for (int k = 0; k < kSweep; ++k) {
+        sv[k] = sv_next[k];
+        cin[k] = cin_next[k];
+      }
     }
     c_total = block_sum_u64<NT>(part, sh);
-    cd = double(c_total);
+    if (c_total) cd = make_divisor(double(c_total));
     if (one_seg) {  // the mixed masses' total and must-keep share
       part = 0;
       mk_part = 0;
@@ -669,30 +750,66 @@ __global__ __launch_bounds__(NT) void k_mass_segment(
         sp += room < cyc ? room : cyc;
       }
       const int64_t r = need - block_sum_i64<NT>(sp, sh);
-      // New quotas go to the output array; the ranks read the old rooms,
-      // which nothing writes during this loop.
-      for (int s = tid; s < ns; s += NT) {
-        const int64_t room = room_of(s);
-        int64_t delta = room < cyc ? room : cyc;
-        if (room > cyc && r > 0) {
-          const uint64_t ms = m_of(s);
-          int64_t rank = 0;
-          if (staged) {  // every thread reads the same entry: LDS broadcasts, no branches
-            int o = 0;
-            for (; o + 4 <= ns; o += 4)
+      if (staged) {
+        // The walk order as one unsigned key per segment: 1 + the mass
+        // (adding: larger first) or 1 + (2^63 - 1 - mass) (removing: smaller
+        // first), and 0 for a segment whose room the full cycles used up.
+        // Masses stay below 2^63 (usage totals are bounded by the window and
+        // pooling, mixed masses sum to about 2^44), so no key wraps.  A tie
+        // goes to the lower index when adding and to the higher one when
+        // removing, so segment s is preceded by o iff key[o] >= key[s] on the
+        // winning side of s and key[o] >= key[s] + 1 on the other.  Keys are
+        // padded with zeros to whole chunks of 32.
+        for (int s = tid; s < ((ns + 31) & ~31); s += NT) {
+          uint64_t key = 0;
+          if (s < ns && sh.u.walk.room[s] > cyc)
+            key = 1 + (adding ? sh.u.walk.m[s] : 0x7fffffffffffffffull - sh.u.walk.m[s]);
+          sh.u.walk.m[s] = key;
+        }
+        __syncthreads();
+        const uint64_t* key = sh.u.walk.m;
+        const int lane = tid & 63;
+        for (int sb = tid - lane; sb < ns; sb += NT) {  // lane s = sb + lane, uniform per wave
+          const int s = sb + lane;
+          const bool mine = s < ns;
+          const int64_t room = mine ? sh.u.walk.room[s] : 0;
+          const uint64_t ks = mine ? key[s] : 0;
+          const bool part = mine && room > cyc && r > 0;
+          const uint64_t t_lo = adding ? ks : ks + 1;  // for o < s
+          const uint64_t t_hi = adding ? ks + 1 : ks;  // for o > s
+          int rank = 0;
+          for (int c = 0; c < ns && __any(part && rank < r); c += 32) {
+            if (c + 32 <= sb || c >= sb + 64) {  // the whole chunk lies on one side of every lane
+              const uint64_t th = c < sb ? t_lo : t_hi;
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                rank += (sh.u.walk.room[o + i] > cyc) &
-                        precedes(sh.u.walk.m[o + i], o + i, ms, s, adding);
-            for (; o < ns; ++o)
-              rank += (sh.u.walk.room[o] > cyc) & precedes(sh.u.walk.m[o], o, ms, s, adding);
-          } else {
+              for (int i = 0; i < 32; ++i) rank += key[c + i] >= th;
+            } else {
+#pragma unroll 4
+              for (int i = 0; i < 32; ++i) {
+                const int o = c + i;
+                rank += (o != s) & (key[o] >= (o < s ? t_lo : t_hi));
+              }
+            }
+          }
+          int64_t delta = room < cyc ? room : cyc;
+          if (part && rank < r) ++delta;
+          if (mine) seg_quota[so + s] = int32_t(adding ? seg_q[so + s] + delta : seg_q[so + s] - delta);
+        }
+      } else {
+        // New quotas go to the output array; the ranks read the old rooms,
+        // which nothing writes during this loop.
+        for (int s = tid; s < ns; s += NT) {
+          const int64_t room = room_of(s);
+          int64_t delta = room < cyc ? room : cyc;
+          if (room > cyc && r > 0) {
+            const uint64_t ms = m_of(s);
+            int64_t rank = 0;
             for (int o = 0; o < ns && rank < r; ++o)
               if (room_of(o) > cyc && precedes(m_of(o), o, ms, s, adding)) ++rank;
+            if (rank < r) ++delta;
           }
-          if (rank < r) ++delta;
+          seg_quota[so + s] = int32_t(adding ? seg_q[so + s] + delta : seg_q[so + s] - delta);
         }
-        seg_quota[so + s] = int32_t(adding ? seg_q[so + s] + delta : seg_q[so + s] - delta);
       }
       if (tid == 0) n_seg[n] = ns;
       return;
