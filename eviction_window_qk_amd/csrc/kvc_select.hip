@@ -23,6 +23,7 @@ constexpr int kMaxWaves = 16;
 constexpr int kCached = 16;    // keys per thread kept in registers by the threshold search
 constexpr int kWaveSeg = 256;  // segments up to this length: one wave each
 constexpr int kPerLane = kWaveSeg / 64;
+constexpr int kSmallQuota = 8;  // one-wave segments with quotas up to this walk the top keys
 
 // LDS of one workgroup of NT threads: the keep bitmap (the short-cache
 // variant only takes caches below 4096 positions, so its bitmap is small and
@@ -262,6 +263,17 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   return min(min(a, b), min(c, d));
 }
 
+// Maximum over the wave's 64 lanes, uniform result (as wave_min_u32).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0xb1, 0xf, 0xf, false)));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0x4e, 0xf, 0xf, false)));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0x141, 0xf, 0xf, false)));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0x140, 0xf, 0xf, false)));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return max(max(a, b), max(c, d));
+}
+
 // The 1024-thread variant is held to 64 VGPRs so that two workgroups share a
 // CU (8 waves per SIMD): one workgroup's barriers and LDS rounds then
 // overlap the other's loads (16K-position global select 128 -> 113 us).
@@ -388,11 +400,41 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT >= 1024 ?
         if (ok[e]) set_bit(sh, a + lane + 64 * e);
       continue;
     }
-    // tau: the largest key with at least q members >= it, bit by bit.  Once
-    // exactly q members are >= the candidate, tau is their smallest key and
-    // the remaining bits need no counting.
+    // tau: the largest key with at least q members >= it (the q-th largest
+    // member key, counted with multiplicity).
     uint32_t tau = 0;
     bool exact = false;
+    if (q <= kSmallQuota) {
+      // Small quotas walk the distinct member keys from the top: each round
+      // takes the largest key below the previous one and counts the members
+      // at or above it, so at most q rounds.  A bit-by-bit search needs a
+      // round per bit down to where the q-th and (q+1)-th keys part (about 17
+      // on float scores), and its rounds cost as much: counting is scalar
+      // work either way (ballot population counts), which the SIMD's scalar
+      // issue slot limits.  A zero maximum means only zero keys are left
+      // (non-members carry 0; a member keyed 0 is then a tie at tau = 0).
+      uint32_t bound = 0xffffffffu;
+      bool first = true;
+      for (int round = 0; round < q; ++round) {
+        uint32_t lm = 0;
+#pragma unroll
+        for (int e = 0; e < kPerLane; ++e)
+          if (ok[e] && (first || key[e] < bound) && key[e] > lm) lm = key[e];
+        const uint32_t m = wave_max_u32(lm);
+        if (m == 0) break;
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < kPerLane; ++e) c += wave_count(key[e] >= m);  // m >= 1 > the 0 of non-members
+        if (c >= uint32_t(q)) {
+          tau = m;
+          break;
+        }
+        bound = m;
+        first = false;
+      }
+    } else {
+    // Bit by bit.  Once exactly q members are >= the candidate, tau is their
+    // smallest key and the remaining bits need no counting.
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = tau | (1u << bit);
       uint32_t c = 0;
@@ -405,6 +447,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT >= 1024 ?
           break;
         }
       }
+    }
     }
     if (exact) {
       uint32_t mn = 0xffffffffu;
