@@ -39,11 +39,12 @@ def steps2to5_head(args):
 
 def usage_head(args):
     """fp64 oracle usage of head-event n of a workload, its inputs regenerated
-    here from the seeded generator (optionally with overridden parameters)."""
-    name, n, over = args
+    here from the seeded generator (optionally with overridden parameters and
+    another seed, as for the first event of a chain)."""
+    name, n, over, seed = args
     wl = synth.WORKLOADS[name]
     pd = wl.event_params(**over)
-    hd = synth.gen_head(wl, n, with_v=False)
+    hd = synth.gen_head(wl, n, seed=seed, with_v=False)
     widen = lambda b: synth.bf16_bits_to_f32(b).astype(np.float64)
     return ams.window_usage(widen(hd["q"]), widen(hd["k"]), oracle_params(pd))
 

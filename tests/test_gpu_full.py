@@ -72,12 +72,12 @@ def _every_head_steps2to5(label, pd, p, u_dev: torch.Tensor, kept_dev: torch.Ten
             print(f"[full] {label}: {n + 1}/{NH} heads bit-exact", flush=True)
 
 
-def _every_head_usage(label, name, u_gpu: np.ndarray, pool, over=None):
+def _every_head_usage(label, name, u_gpu: np.ndarray, pool, over=None, seed=None):
     """The window score of every head-event against the fp64 oracle (inputs
     regenerated per head in the workers)."""
     NH = u_gpu.shape[0]
     print(f"[full] {label}: fp64 oracle usage, all {NH} heads", flush=True)
-    args = [(name, n, over or {}) for n in range(NH)]
+    args = [(name, n, over or {}, seed) for n in range(NH)]
     for n, u_ref in enumerate(pool.imap(oracle_workers.usage_head, args, chunksize=4)):
         assert_usage_close(u_gpu[n], u_ref, f"{label} head {n}")
     print(f"[full] {label}: usage within tolerance on every head", flush=True)
@@ -115,7 +115,8 @@ def _steps2to5_sampled(pd, p, u_full: torch.Tensor, u_ref32: dict, credit_in, k_
     return ms
 
 
-def _check_event(name, pd, q, k, v, credit_in, n_prev, heads, label, pool, usage_all=False):
+def _check_event(name, pd, q, k, v, credit_in, n_prev, heads, label, pool, usage_all=False,
+                 seed=None):
     NH = q.shape[0]
     T = pd["T"]
     print(f"[full] {label}: NH={NH} T={T} K={pd['budget']} sampled heads {heads}", flush=True)
@@ -153,7 +154,7 @@ def _check_event(name, pd, q, k, v, credit_in, n_prev, heads, label, pool, usage
     _steps2to5_sampled(pd, p, ev["u"], u_ref32, credit_in, k, v, dk, dv, n_prev, heads)
     print(f"[full] {label}: steps 2-5 bit-exact on sampled heads", flush=True)
     if usage_all:
-        _every_head_usage(label, name, u_gpu, pool, _overrides(name, pd))
+        _every_head_usage(label, name, u_gpu, pool, _overrides(name, pd), seed)
     _every_head_steps2to5(label, pd, p, ev["u"], ev["kept"], credit_in, ev.get("credit_out"),
                           n_prev, pool)
     return ev
@@ -189,7 +190,7 @@ def test_full_qwen7b_t1536_ema_chain(cpu_pool):
     heads = [0, 3333, 7167]
     q0, k0, v0 = gen_all(name, seed=wl.prior_seed)
     ev0 = _check_event(name, pd, q0, k0, v0, None, 0, heads[:1], "qwen7b_t1536_ema event 0",
-                       cpu_pool)
+                       cpu_pool, usage_all=True, seed=wl.prior_seed)
     k_out = host_bits(ev0["k_out"])
     v_out = host_bits(ev0["v_out"])
     credit = host_u64(ev0["credit_out"])
@@ -222,7 +223,7 @@ def test_full_llama8b_t128k(cpu_pool):
     name = "llama8b_t128k"
     q, k, v = gen_all(name, chunk=4)
     ev = _check_event(name, synth.WORKLOADS[name].event_params(), q, k, v, None, 0, [0, 200], name,
-                      cpu_pool)
+                      cpu_pool, usage_all=True)
     assert int(ev["kept"].shape[1]) == 4096
 
 
