@@ -155,3 +155,38 @@ def test_wide_resident_column_sums_agree_with_streamed():
         assert_usage_close(u_gpu[n], ams.window_usage(widen(q[n]), widen(k[n, :T]), op),
                            f"wide resident head {n}")
     print("[case] wide resident pass 2: identical bits, sampled heads within tolerance", flush=True)
+
+
+@pytest.mark.gpu
+def test_split_rows_and_wide_resident_ragged():
+    """A left-padded batch on the long-cache score path: 512 query rows per
+    head over 49152 positions split pass 1 into 24 key ranges (merged by
+    log-sum-exp) and take the twelve-wave LDS-resident pass 2.  Heads whose
+    real length ends inside the first range leave the later ranges empty
+    (their partial normaliser is -inf and adds nothing); sampled heads match
+    the oracle's masked usage and steps 2-5."""
+    import numpy as np
+    import torch
+    from oracle import ams
+    from parity_utils import (assert_usage_close, check_steps2to5_ragged, dev_bf16, kvc_params,
+                              oracle_params, widen)
+    NH, G, W, d, T, K = 16, 4, 128, 64, 49152, 2000
+    rng = np.random.default_rng(4242)
+    lengths = rng.integers(W, T + 1, size=NH).astype(np.int32)
+    lengths[:4] = [T, 1000, W, 30000 + 17]   # 1000 < one range of 2048 keys
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
+    q, k, v = synth.random_small(9090, NH, G, W, d, T)
+    p = kvc_params(pd, NH)
+    p.valid_len = torch.from_numpy(lengths).cuda()
+    print(f"[case] split pass 1 + wide pass 2, ragged: NH={NH} G={G} W={W} d={d} T={T}", flush=True)
+    u = torch.full((NH, T), float("nan"), dtype=torch.float32, device="cuda")
+    kvc.score_window(p, dev_bf16(q), dev_bf16(k), u=u)
+    u_gpu = u.cpu().numpy()
+    assert not np.isnan(u_gpu).any()
+    op = oracle_params(pd)
+    heads = [0, 1, 2, 3]
+    for n in heads:
+        u_ref = ams.window_usage_ragged(widen(q[n]), widen(k[n, :T]), op, int(lengths[n]))
+        assert_usage_close(u_gpu[n], u_ref, f"split/wide ragged head {n} (len {lengths[n]})")
+    check_steps2to5_ragged(pd, u_gpu, k, v, None, heads, lengths)
+    print("[case] split pass 1 + wide pass 2, ragged: sampled heads ok", flush=True)
