@@ -190,3 +190,34 @@ def test_split_rows_and_wide_resident_ragged():
         assert_usage_close(u_gpu[n], u_ref, f"split/wide ragged head {n} (len {lengths[n]})")
     check_steps2to5_ragged(pd, u_gpu, k, v, None, heads, lengths)
     print("[case] split pass 1 + wide pass 2, ragged: sampled heads ok", flush=True)
+
+
+@pytest.mark.gpu
+def test_whole_head_wide_pass_agrees_with_streamed():
+    """With 256 heads the twelve-wave pass 2 walks a whole head per workgroup,
+    after a pass 1 split into four key ranges.  The same heads launched four at
+    a time take the streamed pass 2 (the same four key ranges, merged the same
+    way); the usage must have the same bits, and sampled heads match the
+    oracle."""
+    import numpy as np
+    import torch
+    from oracle import ams
+    from parity_utils import assert_usage_close, dev_bf16, kvc_params, oracle_params, widen
+    NH, G, W, d, T, K = 256, 4, 128, 64, 8192, 1000
+    pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
+    q, k, _ = synth.random_small(6060, NH, G, W, d, T)
+    dq, dk = dev_bf16(q), dev_bf16(k)
+    print(f"[case] whole-head wide pass: NH={NH} G={G} W={W} d={d} T={T}", flush=True)
+    u_all = kvc.score_window(kvc_params(pd, NH), dq, dk)
+    for sub in ([0, 1, 2, 3], [100, 200, 254, 255]):
+        idx = torch.tensor(sub, device="cuda")
+        u_sub = kvc.score_window(kvc_params(pd, len(sub)), dq[idx].contiguous(), dk[idx].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(u_sub.view(torch.int32), u_all[idx].view(torch.int32)), sub
+    u_gpu = u_all.cpu().numpy()
+    op = oracle_params(pd)
+    for n in (0, 255):
+        assert_usage_close(u_gpu[n], ams.window_usage(widen(q[n]), widen(k[n, :T]), op),
+                           f"whole-head wide pass head {n}")
+    print("[case] whole-head wide pass: identical bits, sampled heads within tolerance",
+          flush=True)
