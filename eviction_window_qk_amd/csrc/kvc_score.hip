@@ -15,19 +15,24 @@
 //   k_rowstats  rows stationary: each wave keeps 64 query rows in registers
 //               (the B operand) and the workgroup streams every key of the
 //               head through double-buffered LDS tiles.  The accumulator gives
-//               each lane one row and 16 keys, so the running max m and sum l
-//               of 2^(x-m), x = <q,k>*scale*log2(e), stay lane-local; the two
-//               lane halves merge once at the end.  Output: the row
-//               normaliser b = m + log2(l) (log2 domain).  When a launch
-//               has too few heads to fill the chip, each head's keys are
-//               split into ranges whose partial normalisers k_rowmerge
-//               combines (b = log2 sum_s 2^b_s).
+//               each lane one row and 16 keys, so the sum l of 2^(x-ref),
+//               x = <q,k>*scale*log2(e), against a lazily kept reference ref
+//               stays lane-local; the two lane halves merge once at the end.
+//               Output: the row normaliser b = ref + log2(l) (log2 domain).
+//               When a launch has too few heads to fill the chip, each head's
+//               keys are split into ranges whose partial normalisers
+//               k_rowmerge combines (b = log2 sum_s 2^b_s).
 //   k_colsum    keys stationary: each wave keeps 64 keys in registers (the B
 //               operand) and the workgroup streams the query rows through
 //               double-buffered LDS.  The accumulator gives each lane one key
 //               and 16 rows, so p = 2^(x - b) summed down the rows is
 //               lane-local; the halves merge at the end (per query head for
 //               the MAX aggregation).
+//   k_colsum_resident
+//               the same column sums with the whole window (queries and
+//               normalisers) resident in LDS, each wave walking chunks of
+//               keys without barriers: four waves for windows of at most four
+//               32-row blocks, twelve (one workgroup per CU) for up to sixteen.
 //   k_fill      positions seen by fewer than W queries take the maximum over
 //               the fully observed ones.
 //
