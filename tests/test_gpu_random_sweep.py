@@ -1,0 +1,99 @@
+"""Seeded random sweep of small events on the GPU against the oracle.
+
+Each case draws a shape and a parameter set the host accepts: group size,
+window, head dim, cache length (on both sides of the 4096-position switch to
+the long-cache kernels), budget (also at or above the cache length), mass
+cut spacing, segment bounds, must-keep sizes, pooling kernel and mode, head
+aggregation, EMA, quota mode, fixed-length segments and, for some cases, a
+left-padded batch.  Every head is held to the same bars as the hand-picked
+parity cases: usage within 2e-3 of the fp64 oracle, steps 2-5 bit for bit on
+the oracle's usage, and the whole event equal to the stages run in turn.
+"""
+import numpy as np
+import pytest
+
+from eviction_window_qk_amd import kvc, synth
+from oracle import ams
+from parity_utils import (assert_usage_close, check_steps2to5_ragged, dev_bf16, kvc_params,
+                          oracle_params, widen)
+from test_gpu_parity import _pd, _run_case
+
+N_CASES = 200
+
+
+def _draw(seed: int):
+    """A valid (pd, NH, lengths or None) for this seed."""
+    rng = np.random.default_rng(1000 + seed)
+    while True:
+        G = int(rng.choice([1, 2, 3, 4, 7, 8]))
+        W = int(rng.choice([1, 5, 16, 32, 33, 64, 128]))
+        d = int(rng.choice([64, 128]))
+        T = int(rng.integers(max(W, 40), 9000)) if rng.random() < 0.6 else int(rng.integers(max(W, 8), 600))
+        K = int(rng.integers(1, T + 50))
+        seg_min = int(rng.choice([1, 4, 16]))
+        seg_max = int(rng.choice([0, 2 * seg_min, 64, 256]))
+        over = dict(
+            group=G, window=W, head_dim=d, T=T, budget=K,
+            delta=float(rng.choice([0.1, 0.05, 0.2, 0.3, 1.0])),
+            seg_min=seg_min, seg_max=seg_max, q_min=int(rng.integers(0, 3)),
+            sinks=int(rng.choice([0, 4])), recent=int(rng.choice([0, 16, 64])),
+            pool_kernel=int(rng.choice([1, 3, 7, 9])), pool_mode=int(rng.integers(0, 2)),
+            head_agg=int(rng.integers(0, 2)), ema=bool(rng.random() < 0.4),
+            quota_mode=int(rng.random() < 0.2),
+            seg_fixed=int(rng.choice([0, 0, 0, 8, 48])),
+        )
+        pd = _pd(**over)
+        NH = int(rng.integers(1, 4))
+        p = kvc_params(pd, NH)
+        if kvc.check_params(p) != 0:
+            continue
+        lengths = None
+        if rng.random() < 0.3:
+            lengths = rng.integers(W, T + 1, size=NH).astype(np.int32)
+        return pd, NH, lengths
+
+
+def test_sweep_draws_are_varied():
+    """The draws reach both kernel sizes, the no-eviction case, every
+    pooling/aggregation mode, EMA, the ablations and ragged batches."""
+    seen = set()
+    for s in range(N_CASES):
+        pd, NH, lengths = _draw(s)
+        seen.add("long" if pd["T"] >= 4096 else "short")
+        seen.add("noop" if pd["budget"] >= pd["T"] else "evict")
+        seen.add(f"pool{pd['pool_mode']}")
+        seen.add(f"agg{pd['head_agg']}")
+        seen.add("ema" if pd["ema"] else "no_ema")
+        if pd["quota_mode"]:
+            seen.add("uniform")
+        if pd["seg_fixed"]:
+            seen.add("fixed")
+        if lengths is not None:
+            seen.add("ragged")
+    need = {"long", "short", "noop", "evict", "pool0", "pool1", "agg0", "agg1", "ema", "no_ema",
+            "uniform", "fixed", "ragged"}
+    assert need <= seen, need - seen
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_event(seed):
+    pd, NH, lengths = _draw(seed)
+    G, W, d, T = pd["group"], pd["window"], pd["head_dim"], pd["T"]
+    label = f"sweep {seed}"
+    q, k, v = synth.random_small(77000 + seed, NH, G, W, d, T)
+    if lengths is None:
+        _run_case(pd, q, k, v, label=label)
+        return
+    import torch
+    print(f"[case] {label} ragged NH={NH} G={G} W={W} d={d} T={T} K={pd['budget']} "
+          f"lengths={lengths.tolist()}", flush=True)
+    p = kvc_params(pd, NH)
+    p.valid_len = torch.from_numpy(lengths).cuda()
+    u = kvc.score_window(p, dev_bf16(q), dev_bf16(k)).cpu().numpy()
+    op = oracle_params(pd)
+    u_ref = np.zeros((NH, T), dtype=np.float64)
+    for n in range(NH):
+        u_ref[n] = ams.window_usage_ragged(widen(q[n]), widen(k[n, :T]), op, int(lengths[n]))
+        assert_usage_close(u[n], u_ref[n], f"{label} head {n} (len {lengths[n]})")
+    check_steps2to5_ragged(pd, u_ref.astype(np.float32), k, v, None, range(NH), lengths)
