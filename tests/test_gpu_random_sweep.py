@@ -4,8 +4,9 @@ Each case draws a shape and a parameter set the host accepts: group size,
 window, head dim, cache length (on both sides of the 4096-position switch to
 the long-cache kernels), budget (also at or above the cache length), mass
 cut spacing, segment bounds, must-keep sizes, pooling kernel and mode, head
-aggregation, EMA, quota mode, fixed-length segments and, for some cases, a
-left-padded batch.  Every head is held to the same bars as the hand-picked
+aggregation, EMA (fresh, or with credit carried from an earlier event), quota
+mode, fixed-length segments, a key/value row stride past the cache length
+and, for some cases, a left-padded batch.  Every head is held to the same bars as the hand-picked
 parity cases: usage within 2e-3 of the fp64 oracle, steps 2-5 bit for bit on
 the oracle's usage, and the whole event equal to the stages run in turn.
 """
@@ -22,7 +23,7 @@ N_CASES = 200
 
 
 def _draw(seed: int):
-    """A valid (pd, NH, lengths or None) for this seed."""
+    """A valid (pd, NH, lengths or None, n_prev, t_stride) for this seed."""
     rng = np.random.default_rng(1000 + seed)
     while True:
         G = int(rng.choice([1, 2, 3, 4, 7, 8]))
@@ -48,9 +49,25 @@ def _draw(seed: int):
         if kvc.check_params(p) != 0:
             continue
         lengths = None
+        n_prev, t_stride = 0, T
         if rng.random() < 0.3:
             lengths = rng.integers(W, T + 1, size=NH).astype(np.int32)
-        return pd, NH, lengths
+        else:
+            if pd["ema"] and rng.random() < 0.5:
+                n_prev = int(rng.integers(1, T + 1))
+            if rng.random() < 0.3:
+                t_stride = T + int(rng.integers(1, 40))
+        if kvc.check_params(kvc_params(pd, NH, n_prev, t_stride)) != 0:
+            continue
+        return pd, NH, lengths, n_prev, t_stride
+
+
+def _credit(seed: int, NH: int, n_prev: int) -> np.ndarray:
+    """Carried credit like an earlier event's output: Q44 fractions summing to
+    about 2^44 per head."""
+    rng = np.random.default_rng(5000 + seed)
+    r = rng.random((NH, n_prev)) ** 3 + 1e-3
+    return np.floor(r / r.sum(axis=1, keepdims=True) * 2.0 ** 44).astype(np.uint64)
 
 
 def test_sweep_draws_are_varied():
@@ -58,7 +75,7 @@ def test_sweep_draws_are_varied():
     pooling/aggregation mode, EMA, the ablations and ragged batches."""
     seen = set()
     for s in range(N_CASES):
-        pd, NH, lengths = _draw(s)
+        pd, NH, lengths, n_prev, t_stride = _draw(s)
         seen.add("long" if pd["T"] >= 4096 else "short")
         seen.add("noop" if pd["budget"] >= pd["T"] else "evict")
         seen.add(f"pool{pd['pool_mode']}")
@@ -70,20 +87,25 @@ def test_sweep_draws_are_varied():
             seen.add("fixed")
         if lengths is not None:
             seen.add("ragged")
+        if n_prev:
+            seen.add("carried_credit")
+        if t_stride > pd["T"]:
+            seen.add("stride")
     need = {"long", "short", "noop", "evict", "pool0", "pool1", "agg0", "agg1", "ema", "no_ema",
-            "uniform", "fixed", "ragged"}
+            "uniform", "fixed", "ragged", "carried_credit", "stride"}
     assert need <= seen, need - seen
 
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_event(seed):
-    pd, NH, lengths = _draw(seed)
+    pd, NH, lengths, n_prev, t_stride = _draw(seed)
     G, W, d, T = pd["group"], pd["window"], pd["head_dim"], pd["T"]
     label = f"sweep {seed}"
-    q, k, v = synth.random_small(77000 + seed, NH, G, W, d, T)
+    q, k, v = synth.random_small(77000 + seed, NH, G, W, d, T, t_stride=t_stride)
     if lengths is None:
-        _run_case(pd, q, k, v, label=label)
+        credit = _credit(seed, NH, n_prev) if n_prev else None
+        _run_case(pd, q, k, v, credit_in=credit, n_prev=n_prev, t_stride=t_stride, label=label)
         return
     import torch
     print(f"[case] {label} ragged NH={NH} G={G} W={W} d={d} T={T} K={pd['budget']} "
