@@ -47,6 +47,27 @@ CASES = [
 ]
 
 
+def _random_cases(n):
+    """Seeded random layouts: batch size, KV heads, cache length, block size
+    (odd sizes and single-slot blocks included), head dim, budget, separate
+    output pools, empty kept slots and skipped destination blocks."""
+    rng = np.random.default_rng(2024)
+    out = []
+    for i in range(n):
+        T = int(rng.integers(2, 1200))
+        kw = dict(same_pool=bool(rng.random() < 0.5), empty=bool(rng.random() < 0.3))
+        B = int(rng.integers(2, 6))
+        if kw["empty"] or rng.random() < 0.3:
+            kw["bad_ids"] = bool(rng.random() < 0.5)
+        out.append((f"random{i}", B, int(rng.choice([1, 2, 4, 8])), T,
+                    int(rng.choice([1, 2, 3, 7, 8, 16, 32, 64])), int(rng.choice([64, 128])),
+                    int(rng.integers(8, T + 1)) if T >= 8 else T, kw))
+    return out
+
+
+CASES += _random_cases(24)
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_gather_paged_matches_oracle(case):
     label, B, H, T, bs, d, K, kw = case
@@ -66,12 +87,15 @@ def test_gather_paged_matches_oracle(case):
     n_blocks = k_pool.shape[0]
     ok_rows = np.ones_like(kept, dtype=bool)
     tout_ok = tout.copy()
+    # Rows with a skipped destination go to a spare block that neither table
+    # names, so the oracle's copy of them cannot land on a real destination.
+    spare = min(set(range(n_blocks)) - set(tin.ravel().tolist()) - set(tout.ravel().tolist()))
     for b in range(B):
         for j in range(K):
             blk = tout[b, j // bs]
             if blk < 0 or blk >= n_blocks:
                 ok_rows[b * H:(b + 1) * H, j] = False
-                tout_ok[b, j // bs] = 0
+                tout_ok[b, j // bs] = spare
     want_k, want_v = base_k.copy(), base_v.copy()
     ref_k, ref_v = ams.gather_paged(kept, k_pool, v_pool, tin, tout_ok, H)
     for n in range(B * H):
