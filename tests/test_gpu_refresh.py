@@ -42,16 +42,35 @@ def test_qc_trigger_matches_oracle():
     assert full_o.any() and (~full_o).any()
 
 
-@pytest.mark.parametrize("d", [128, 64])
-def test_partial_loop_and_sync_match_oracle(d):
-    NH, K, T0, steps = 24, 64, 700, 40
-    rng = np.random.default_rng(d)
+def _random_loops(n):
+    """Seeded random decode loops: head count, cache budget (one slot up),
+    cache length, steps (more steps than slots included, so every slot turns
+    over), head dim, empty slots on one head and the spacing of tied scores."""
+    rng = np.random.default_rng(909)
+    out = []
+    for i in range(n):
+        K = int(rng.integers(1, 300))
+        out.append((f"random{i}", int(rng.integers(1, 40)), K, int(rng.integers(K, 2000)),
+                    int(rng.integers(1, 2 * K + 20)), int(rng.choice([64, 128])),
+                    int(rng.integers(0, K + 1)), int(rng.choice([1, 3, 50]))))
+    return out
+
+
+LOOPS = [("d128", 24, 64, 700, 40, 128, 5, 50), ("d64", 24, 64, 700, 40, 64, 5, 50)] + _random_loops(12)
+
+
+@pytest.mark.parametrize("case", LOOPS, ids=[c[0] for c in LOOPS])
+def test_partial_loop_and_sync_match_oracle(case):
+    label, NH, K, T0, steps, d, n_empty, tie_step = case
+    print(f"[case] refresh loop {label}: NH={NH} K={K} T0={T0} steps={steps} d={d}", flush=True)
+    rng = np.random.default_rng(sum(map(ord, label)) + d)
     kf = synth.f32_to_bf16_bits(rng.standard_normal((NH, T0 + steps, d), dtype=np.float32))
     vf = synth.f32_to_bf16_bits(rng.standard_normal((NH, T0 + steps, d), dtype=np.float32))
     kept = np.stack([np.sort(rng.choice(T0, K, replace=False)) for _ in range(NH)]).astype(np.int32)
-    kept[3, -5:] = -1                                       # a short head: empty slots
+    if n_empty:
+        kept[NH // 2, K - n_empty:] = -1                    # a short head: empty slots
     score = rng.random((NH, T0)).astype(np.float32)
-    score[:, ::50] = 0.25                                   # ties
+    score[:, ::tie_step] = 0.25                             # ties
     new_k = synth.f32_to_bf16_bits(rng.standard_normal((steps, NH, d), dtype=np.float32))
     new_v = synth.f32_to_bf16_bits(rng.standard_normal((steps, NH, d), dtype=np.float32))
     # oracle
