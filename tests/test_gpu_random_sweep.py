@@ -119,3 +119,60 @@ def test_random_event(seed):
         u_ref[n] = ams.window_usage_ragged(widen(q[n]), widen(k[n, :T]), op, int(lengths[n]))
         assert_usage_close(u[n], u_ref[n], f"{label} head {n} (len {lengths[n]})")
     check_steps2to5_ragged(pd, u_ref.astype(np.float32), k, v, None, range(NH), lengths)
+
+
+N_LONG = 20
+
+
+def _draw_long(seed: int):
+    """A valid long-cache case: enough heads and positions for the resident
+    and twelve-wave column sums and the split row statistics."""
+    rng = np.random.default_rng(3000 + seed)
+    while True:
+        NH = int(rng.choice([16, 32, 64, 128]))
+        T = int(rng.integers(8192, 40000))
+        if NH * T > 2_200_000:
+            continue
+        G = int(rng.choice([1, 2, 4, 8]))
+        W = int(rng.choice([16, 32, 64, 128]))
+        if seed % 5 == 0:  # a launch with >= 8192 column-sum chunks and a small window: resident pass 2
+            NH, T = 128, int(rng.integers(16384, 17000))
+            G, W = int(rng.choice([1, 2, 4])), int(rng.choice([16, 32]))
+        seg_min = int(rng.choice([4, 16]))
+        over = dict(
+            group=G, window=W, head_dim=int(rng.choice([64, 128])), T=T,
+            budget=int(rng.integers(64, T // 4)),
+            delta=float(rng.choice([0.1, 0.05, 1.0])), seg_min=seg_min,
+            seg_max=int(rng.choice([0, 4 * seg_min, 256])), q_min=int(rng.integers(0, 3)),
+            sinks=4, recent=64, pool_kernel=int(rng.choice([3, 7])),
+            pool_mode=int(rng.integers(0, 2)), head_agg=int(rng.random() < 0.25),
+            ema=bool(rng.random() < 0.4), quota_mode=int(rng.random() < 0.2),
+        )
+        pd = _pd(**over)
+        if kvc.check_params(kvc_params(pd, NH)) != 0:
+            continue
+        return pd, NH
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", range(N_LONG))
+def test_random_long_event(seed):
+    import torch
+    from parity_utils import check_event_consistency, check_steps2to5
+    pd, NH = _draw_long(seed)
+    G, W, d, T = pd["group"], pd["window"], pd["head_dim"], pd["T"]
+    heads = sorted({0, NH // 2, NH - 1})
+    print(f"[case] long sweep {seed}: NH={NH} G={G} W={W} d={d} T={T} K={pd['budget']} "
+          f"agg={pd['head_agg']} ema={pd['ema']} sampled heads {heads}", flush=True)
+    q, k, v = synth.random_small(88000 + seed, NH, G, W, d, T)
+    dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    p = kvc_params(pd, NH)
+    u_gpu = kvc.score_window(p, dq, dk).cpu().numpy()
+    op = oracle_params(pd)
+    u_mix = u_gpu.copy()
+    for n in heads:
+        u_ref = ams.window_usage(widen(q[n]), widen(k[n, :T]), op)
+        assert_usage_close(u_gpu[n], u_ref, f"long sweep {seed} head {n}")
+        u_mix[n] = u_ref.astype(np.float32)
+    check_steps2to5(pd, u_mix, k, v, None, heads, dk=dk, dv=dv)
+    check_event_consistency(pd, dq, dk, dv, None, NH)
