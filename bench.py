@@ -522,7 +522,7 @@ def main():
                       else {})},
         "roofline": {**roof,
                      "traffic": None if (args.ragged or variant) else recorded_traffic(wl.name),
-                     "kernel": "score stage (k_rowstats + k_colsum + k_fill)",
+                     "kernel": "score stage (k_rowstats [+ k_rowmerge] + k_colsum or k_colsum_resident + k_fill)",
                      "algorithmic_flops_per_launch": alg["flops"],
                      "algorithmic_bytes_per_launch": alg["b_score"],
                      "mfma_frac": achieved / PEAK_BF16_TFLOPS},
