@@ -57,3 +57,26 @@ def test_noalloc_rejects_an_event_past_its_scratch():
     assert kvc.workspace_bytes(p) > kvc.NOALLOC_SCRATCH_BYTES
     rc = kvc.lib().kvc_compress_event_noalloc(ctypes.byref(p.to_c()), *([None] * 10))
     assert rc == kvc.ESCRATCH
+
+
+def test_noalloc_sequence_of_varied_events():
+    """Ten events in a row through the no-allocation entry point, each a
+    different shape and parameter set (seeded draws of the random sweep:
+    pooling, aggregation, EMA with and without carried credit, ablations,
+    row stride), each bit for bit equal to the workspace entry point: no call
+    depends on what an earlier one left in the shared scratch."""
+    from test_gpu_random_sweep import _credit, _draw
+    done = 0
+    seed = 0
+    while done < 10:
+        pd, NH, lengths, n_prev, t_stride = _draw(seed)
+        seed += 1
+        if lengths is not None or t_stride != pd["T"]:
+            continue
+        G, W, d, T = pd["group"], pd["window"], pd["head_dim"], pd["T"]
+        q, k, v = synth.random_small(99000 + seed, NH, G, W, d, T)
+        credit = _credit(seed, NH, n_prev) if n_prev else None
+        print(f"[noalloc] sequence call {done}: NH={NH} G={G} W={W} d={d} T={T} K={pd['budget']} "
+              f"ema={pd['ema']} n_prev={n_prev}", flush=True)
+        _both(pd, NH, q, k, v, credit, n_prev)
+        done += 1
