@@ -126,7 +126,7 @@ static int derive(const kvc_params* p, Derived* d) {
       p->seg_fixed > 0 ? int((int64_t(p->T) + p->seg_fixed - 1) / p->seg_fixed) - 1 : n_thr;
   d->n_thr = n_cut;
   d->seg_fixed = p->seg_fixed;
-  d->rs_split = score_pass1_splits(d->NH, d->R, d->T);
+  d->rs_split = score_pass1_splits(d->R, d->T);  // sized for the longest head
   d->quota_uniform = p->quota_mode == KVC_QUOTA_UNIFORM ? 1 : 0;
   d->vlen = p->valid_len;
   int64_t cap = int64_t(n_cut) + 1 + (p->seg_max > 0 ? p->T / p->seg_max : 0);

@@ -59,24 +59,24 @@ __host__ __device__ __forceinline__ Keep must_keep(int sinks, int recent, int K,
   return Keep{s, r, K - s - r};
 }
 
-// Key ranges the row-statistics pass splits each head's keys into, so that a
-// launch of heads with more than 128 query rows fills the chip: eight rounds
-// of workgroups at three waves per SIMD on the 256 CUs of an MI355X (fewer
-// rounds leave a longer tail; 2 -> 8 rounds: 128K-token event 9.75 -> 9.51
-// ms), in whole 64-key tiles of at least 2048 keys.  Heads with at most 128
-// rows stream K at the copy rate already and are not split (measured no
+// Key ranges the row-statistics pass splits a head's keys into: whole 64-key
+// tiles, about kRangeKeys keys each, for heads with more than 128 query rows
+// (at most 128 rows stream K at the copy rate already and are not split).  The
+// count depends only on the head's own length and row count, never on the
+// launch, so a head's normalisers (and its usage) have the same bits whatever
+// other heads share the launch; a launch sizes its partials for its longest
+// head, and a shorter head leaves its later ranges empty (partial -inf, which
+// adds nothing to the merge).  12 ranges at 131072 keys: with 256 heads of 512
+// rows that is 6144 four-wave workgroups, eight rounds at three waves per SIMD
+// on the 256 CUs of an MI355X (2, 3, 6 ranges measured slower; 18, 24 no
 // faster).  The partial statistics are merged by a log-sum-exp pass.
-inline int score_pass1_splits(int NH, int R, int T) {
-  if (R <= 128 || NH < 1) return 1;
-  const int64_t wgs = int64_t(NH) * ((R + 255) / 256);  // four-wave workgroups of 256 rows
-  const int64_t target = 8 * (256 * 12 / 4);
-  if (wgs >= target) return 1;
-  int64_t s = (target + wgs - 1) / wgs;
-  const int64_t cap = T / 2048 > 1 ? T / 2048 : 1;
-  s = s < cap ? s : cap;
+constexpr int kRangeKeys = 172 * 64;
+__host__ __device__ inline int score_pass1_splits(int R, int T) {
+  if (R <= 128 || T <= kRangeKeys) return 1;
+  int s = (T + kRangeKeys - 1) / kRangeKeys;
   s = s < 64 ? s : 64;
-  const int64_t span = ((T + s - 1) / s + 63) / 64 * 64;  // no range left empty
-  return int((T + span - 1) / span);
+  const int span = ((T + s - 1) / s + 63) / 64 * 64;  // no range left empty
+  return (T + span - 1) / span;
 }
 
 // Workspace carve-up (byte offsets into the caller's buffer, 256-B aligned).

@@ -265,7 +265,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2
   }
 
   // This workgroup's key range: whole tiles, so no tile straddles two ranges.
-  const int span = ((T + S - 1) / S + kRsTile - 1) / kRsTile * kRsTile;
+  // The head splits by its own length (ranges past its count are empty).
+  const int S_head = min(score_pass1_splits(R, T), S);  // never above the launch's (T <= P.T)
+  const int span = ((T + S_head - 1) / S_head + kRsTile - 1) / kRsTile * kRsTile;
   const int t_lo = split * span;
   const int t_hi = t_lo + span < T ? t_lo + span : T;
   const u32x4* kn = k + (size_t(n) * P.TS + sp.off) * kPerRow;

@@ -160,11 +160,12 @@ def test_wide_resident_column_sums_agree_with_streamed():
 @pytest.mark.gpu
 def test_split_rows_and_wide_resident_ragged():
     """A left-padded batch on the long-cache score path: 512 query rows per
-    head over 49152 positions split pass 1 into 24 key ranges (merged by
+    head over 49152 positions split pass 1 into 5 key ranges (merged by
     log-sum-exp) and take the twelve-wave LDS-resident pass 2.  Heads whose
-    real length ends inside the first range leave the later ranges empty
-    (their partial normaliser is -inf and adds nothing); sampled heads match
-    the oracle's masked usage and steps 2-5."""
+    real length is shorter split into fewer ranges of their own (a head of
+    1000 positions into one) and leave the rest empty (their partial
+    normaliser is -inf and adds nothing); sampled heads match the oracle's
+    masked usage and steps 2-5."""
     import numpy as np
     import torch
     from oracle import ams
@@ -173,7 +174,7 @@ def test_split_rows_and_wide_resident_ragged():
     NH, G, W, d, T, K = 16, 4, 128, 64, 49152, 2000
     rng = np.random.default_rng(4242)
     lengths = rng.integers(W, T + 1, size=NH).astype(np.int32)
-    lengths[:4] = [T, 1000, W, 30000 + 17]   # 1000 < one range of 2048 keys
+    lengths[:4] = [T, 1000, W, 30000 + 17]   # 1000: one range
     pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
     q, k, v = synth.random_small(9090, NH, G, W, d, T)
     p = kvc_params(pd, NH)
@@ -195,15 +196,15 @@ def test_split_rows_and_wide_resident_ragged():
 @pytest.mark.gpu
 def test_whole_head_wide_pass_agrees_with_streamed():
     """With 256 heads the twelve-wave pass 2 walks a whole head per workgroup,
-    after a pass 1 split into four key ranges.  The same heads launched four at
-    a time take the streamed pass 2 (the same four key ranges, merged the same
+    after a pass 1 split into two key ranges.  The same heads launched four at
+    a time take the streamed pass 2 (the same two key ranges, merged the same
     way); the usage must have the same bits, and sampled heads match the
     oracle."""
     import numpy as np
     import torch
     from oracle import ams
     from parity_utils import assert_usage_close, dev_bf16, kvc_params, oracle_params, widen
-    NH, G, W, d, T, K = 256, 4, 128, 64, 8192, 1000
+    NH, G, W, d, T, K = 256, 4, 128, 64, 12288, 1000
     pd = _pd(group=G, window=W, head_dim=d, T=T, budget=K)
     q, k, _ = synth.random_small(6060, NH, G, W, d, T)
     dq, dk = dev_bf16(q), dev_bf16(k)
