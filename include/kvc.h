@@ -20,7 +20,9 @@
  *    state between calls and never synchronises: all work is enqueued on
  *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and
  *    completes asynchronously.  Results are deterministic: the same inputs
- *    give the same bits on every run.
+ *    give the same bits on every run, and a head's results do not depend on
+ *    the other heads of the call (a head alone, with T set to its real
+ *    length, gives the bits it gets inside a left-padded batch).
  *  - All arguments are validated on the host before anything is enqueued; on
  *    an error return nothing has been launched and no output was touched.
  *  - Return values: KVC_OK (0), KVC_NOOP (1, informational: T <= budget, so
