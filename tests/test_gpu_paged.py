@@ -65,7 +65,7 @@ def _random_cases(n):
     return out
 
 
-CASES += _random_cases(24)
+CASES += _random_cases(200)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])

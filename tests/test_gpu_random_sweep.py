@@ -19,7 +19,7 @@ from parity_utils import (assert_usage_close, check_steps2to5_ragged, dev_bf16, 
                           oracle_params, widen)
 from test_gpu_parity import _pd, _run_case
 
-N_CASES = 200
+N_CASES = 1000
 
 
 def _draw(seed: int):
@@ -121,7 +121,7 @@ def test_random_event(seed):
     check_steps2to5_ragged(pd, u_ref.astype(np.float32), k, v, None, range(NH), lengths)
 
 
-N_LONG = 20
+N_LONG = 30
 
 
 def _draw_long(seed: int):

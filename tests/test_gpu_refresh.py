@@ -56,7 +56,7 @@ def _random_loops(n):
     return out
 
 
-LOOPS = [("d128", 24, 64, 700, 40, 128, 5, 50), ("d64", 24, 64, 700, 40, 64, 5, 50)] + _random_loops(12)
+LOOPS = [("d128", 24, 64, 700, 40, 128, 5, 50), ("d64", 24, 64, 700, 40, 64, 5, 50)] + _random_loops(60)
 
 
 @pytest.mark.parametrize("case", LOOPS, ids=[c[0] for c in LOOPS])
