@@ -25,6 +25,9 @@
  *    length, gives the bits it gets inside a left-padded batch).
  *  - All arguments are validated on the host before anything is enqueued; on
  *    an error return nothing has been launched and no output was touched.
+ *  - A call enqueues kernel launches only (no memset, copy or allocation), so
+ *    it can be captured into a HIP graph and replayed with new inputs copied
+ *    into the captured buffers.
  *  - Return values: KVC_OK (0), KVC_NOOP (1, informational: T <= budget, so
  *    nothing is evicted), negative = error (see kvc_strerror).
  *  - bf16 tensors are raw IEEE bfloat16; q, k, v, k_out, v_out must be
