@@ -75,6 +75,14 @@ def test_eps_quantum():
     assert list(map(int, w)) == [1099512, 2 ** 40 + 1099512, 1 + 1099512, 7 * 2 ** 39 + 1099512]
 
 
+def test_negative_usage_counts_as_zero():
+    # m_i = (max(u_i, 0) + eps) / sum [AMS notes, key design 1, mass equation]:
+    # a negative (or negative-zero) usage adds exactly the eps quantum, the
+    # same as a zero usage; its magnitude does not count
+    w = ams.usage_fixed(np.array([-1.0, -0.0, 0.0, -2.0 ** -30, 2.0], dtype=np.float32), _p(5))
+    assert list(map(int, w)) == [1099512, 1099512, 1099512, 1099512, 2 ** 41 + 1099512]
+
+
 def test_prefix_is_sequential_sum():
     rng = np.random.default_rng(4)
     v = rng.integers(0, 2 ** 50, size=500).astype(np.uint64)

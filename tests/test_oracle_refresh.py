@@ -46,6 +46,32 @@ def test_trigger_updates_reference_only_when_it_fires():
     assert cos[0] == pytest.approx(1.0, abs=1e-12) and cos[1] == pytest.approx(-1.0, abs=1e-12)
 
 
+def test_trigger_only_strictly_below_the_threshold():
+    # [RefreshKV notes, A2: a layer whose similarity falls below s takes a full
+    # step] cos((3,4), (4,3)) = 24/25 exactly: at s = 0.96 the row is not below
+    # the threshold, at the next double above it is
+    q = np.array([[[3.0, 4.0]]])
+    ref = np.array([[4.0, 3.0]])
+    full, cos, _ = refresh.qc_trigger(q, ref, 0.96)
+    assert cos[0] == 0.96 and not full[0]
+    full, _, _ = refresh.qc_trigger(q, ref, np.nextafter(0.96, 1.0))
+    assert full[0]
+
+
+def test_untriggered_steps_keep_comparing_with_the_last_full_step():
+    # the reference is the query of the layer's last full step: a step that
+    # does not trigger leaves it in place, so a slow drift is measured from
+    # the last full step, not from the previous token
+    ref = np.array([[1.0, 0.0]])
+    full1, _, ref1 = refresh.qc_trigger(np.array([[[1.0, 0.1]]]), ref, 0.75)    # cos 0.995
+    assert not full1[0]
+    np.testing.assert_array_equal(ref1, ref)
+    full2, cos2, ref2 = refresh.qc_trigger(np.array([[[0.7, 0.7]]]), ref1, 0.75)
+    assert cos2[0] == pytest.approx(np.sqrt(0.5), abs=1e-15)    # against (1, 0), not (1, 0.1)
+    assert full2[0]
+    np.testing.assert_array_equal(ref2[0], [0.7, 0.7])
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_never_refreshed_partial_cache_is_snapkv(seed):
     # After m partial steps without a refresh, the prompt tokens still in C_p

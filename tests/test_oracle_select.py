@@ -140,6 +140,16 @@ def test_quota_hand_cases():
     assert list(_quota_case([3, 1], 2 + 8)) == [7, 3]
 
 
+def test_quota_excess_never_goes_below_a_floor():
+    # masses 1:5:5:5, floors 1 each, T_rem = 2: shares 0.125 -> 0 and 0.625 -> 1
+    # three times, one slot too many.  The excess comes back in (mass asc,
+    # index desc) order from segments still above their floor: the light
+    # segment sits at its floor and is passed over, the last heavy one gives
+    # the slot back [AMS notes, key design 3: clip and redistribute, floors
+    # held while the budget allows] -> (1, 2, 2, 1), not (0, 2, 2, 2)
+    assert list(_quota_case([1, 5, 5, 5], 4 + 2)) == [1, 2, 2, 1]
+
+
 def test_quota_clip_and_redistribute():
     # the heavy segment (length 10) asks for more than it has; the rest goes
     # to the others in mass order

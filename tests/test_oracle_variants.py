@@ -190,6 +190,28 @@ def test_ragged_budget_invariants(length):
     np.testing.assert_array_equal(res.score[:off], 0.0)
 
 
+@pytest.mark.parametrize("length", [20, 37, 60])
+def test_ragged_carried_credit_covers_only_real_tokens(length):
+    # credit_in[j] belongs to real token j [AMS notes, key design 1: credit
+    # follows the kept positions]; a head shorter than the carried credit is
+    # the plain event on its real tokens with the first `length` credits
+    rng = np.random.default_rng(length)
+    T, W, K, n_prev = 120, 8, 16, 37
+    p = ams.Params(T=T, window=W, budget=K, seg_min=4, seg_max=16, ema=True, n_prev=n_prev)
+    u = (rng.random(T) ** 2).astype(np.float32)
+    r = rng.random(n_prev) + 1e-3
+    credit = np.floor(r / r.sum() * 2.0 ** 44).astype(np.uint64)
+    z = np.zeros((T, 2), np.uint16)
+    res = ams.steps2to5_ragged(u, z, z, credit, p, length)
+    off = T - length
+    ref = ams.steps2to5(u[off:], z[off:], z[off:], credit[:min(n_prev, length)],
+                        p.with_(T=length, n_prev=min(n_prev, length)))
+    np.testing.assert_array_equal(res.credit_upd[off:], ref.credit_upd)
+    np.testing.assert_array_equal(res.credit_upd[:off], 0)
+    np.testing.assert_array_equal(res.kept, np.where(ref.kept >= 0, ref.kept + off, -1))
+    np.testing.assert_array_equal(res.credit_out, ref.credit_out)
+
+
 def test_ragged_clamps_short_lengths_to_the_window():
     rng = np.random.default_rng(3)
     p = ams.Params(T=64, window=16, budget=8, seg_min=4, seg_max=16)
