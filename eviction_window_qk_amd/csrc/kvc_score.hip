@@ -387,7 +387,13 @@ __device__ __forceinline__ void col_update1(const f32x16& a, const float (&b)[16
   cs += s0 + s1;
 }
 
-template <int D>
+// PRIO: the wave runs its softmax arithmetic at raised issue priority
+// (s_setprio), so that on a SIMD shared by waves walking keys without
+// barriers the one in its VALU phase issues first while the others' MFMAs
+// run (128K-token event, twelve-wave resident pass: score stage -1.5 to -2.3 %,
+// same bits; no gain, or a loss within noise, for the kernels that meet at a
+// barrier after every query batch).
+template <int D, bool PRIO = false>
 __device__ __forceinline__ void cs_block(CsCtx<D>& cx, const u32x4* __restrict__ buf, int bi,
                                          const float* __restrict__ bblk, int lim_lo, float c,
                                          int kbase, int j, int h) {
@@ -417,10 +423,12 @@ __device__ __forceinline__ void cs_block(CsCtx<D>& cx, const u32x4* __restrict__
       a1 = mfma32(f[s], cx.kop[1][s], a1);
     }
     load_b();
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
     if (vis0) col_update1<false>(a0, b, c, lim_lo, cx.key0, h, cx.cs0);
     else col_update1<true>(a0, b, c, lim_lo, cx.key0, h, cx.cs0);
     if (vis1) col_update1<false>(a1, b, c, lim_lo, cx.key0 + 32, h, cx.cs1);
     else col_update1<true>(a1, b, c, lim_lo, cx.key0 + 32, h, cx.cs1);
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
   } else {
     f32x16 a0 = f32x16{};
 #pragma unroll
@@ -615,7 +623,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     }
     cx.cs0 = cx.cs1 = 0.0f;
     for (int blk = 0; blk < n_blocks; ++blk)
-      cs_block<D>(cx, qs, blk, bsh + blk * 32, T - W + (blk % n_rb) * 32, c, key_base, j, h);
+      cs_block<D, (NW > kCsWaves)>(cx, qs, blk, bsh + blk * 32, T - W + (blk % n_rb) * 32, c,
+                                   key_base, j, h);
     cx.cs0 += __shfl_xor(cx.cs0, 32);
     cx.cs1 += __shfl_xor(cx.cs1, 32);
     if (h == 0) {
